@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized dense projection on one MI355X.
+
+Headline (the JSON line's ``value``): weight-streaming rate of the row-scaled
+FP8 GEMV on the decode / verify workload -- weight [N, K=5120] E4M3 with a
+per-row F32 scale, BF16 activations, N in {6144, 17408, 152064} and
+M in {1, 2, 8, 16}.  One step runs the GEMV once for every (N, M) pair;
+``value`` = weight bytes read per step (N*K + 4N per call) / step time, in
+GB/s, with every input already resident in HBM.  Weights rotate over copies
+whose total footprint exceeds 1 GiB per shape so that the 256 MB Infinity
+Cache cannot hold them.
+
+The same line carries:
+  roofline      the dominant kernel (the M=16 lm_head GEMV, N=152064) timed
+                alone with HIP events on the launch stream, its algorithmic
+                bytes per launch, and the fraction of the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same step;
+  secondary     every other row of the hot path at its own workload size:
+                quantizers / requantizers in GB/s against HBM, and the three
+                GEMMs in TFLOP/s against the MFMA peak of their data type.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"int8": 5033.0, "fp8": 5033.0, "fp4": 10066.0, "bf16": 2516.6,
+               "fp16": 2516.6}
+METRIC = ("TFLOP/s & %MFMA peak (GEMM M≥2048); weight GB/s & %HBM peak "
+          "(GEMV M≤16)")
+GEMV_SHAPES = [(6144, 5120), (17408, 5120), (152064, 5120)]
+GEMV_MS = [1, 2, 8, 16]
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="GEMV step only")
+    ap.add_argument("--only", default="", help="comma list of secondary items to run")
+    return ap.parse_args()
+
+
+def gemv_bytes(m, n, k):
+    """Algorithmic bytes of one GEMV launch: weight, row scales, activations
+    in, BF16 outputs."""
+    return n * k + 4 * n + 2 * m * k + 2 * m * n
+
+
+def time_launches(fn, iters, warm=2):
+    """Average duration (ms) of `fn` launched back to back on the current
+    stream, measured with HIP events recorded on that stream."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def rot_count(nbytes):
+    return max(2, -(-ROTATE_BYTES // max(1, nbytes)))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemv_nvfp4_int8_amd as qp
+    import synth
+
+    dev = torch.device("cuda:0")
+    qp.lib()
+
+    # ---------------------------------------------------------- GEMV setup
+    log("setting up GEMV weights")
+    weights = {}     # (n,k) -> list of (wq, ws) rotating copies
+    acts = {}
+    for sid, (n, k) in enumerate(GEMV_SHAPES):
+        wb = synth.gemv_weight_bf16(n, k, dev, shape_id=sid)
+        wq = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        ws = torch.empty((n,), dtype=torch.float32, device=dev)
+        qp.quant_rowwise_fp8(wb, wq, ws)
+        del wb
+        copies = [(wq, ws)] + [(wq.clone(), ws.clone()) for _ in range(rot_count(n * k) - 1)]
+        weights[(n, k)] = copies
+        acts[(n, k)] = synth.gemv_acts_bf16(16, k, dev, shape_id=sid)
+    outs = {(n, m): torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            for (n, _) in GEMV_SHAPES for m in GEMV_MS}
+    torch.cuda.synchronize()
+
+    ctr = {"i": 0}
+
+    def step():
+        for (n, k) in GEMV_SHAPES:
+            copies = weights[(n, k)]
+            for m in GEMV_MS:
+                wq, ws = copies[ctr["i"] % len(copies)]
+                ctr["i"] += 1
+                qp.fp8_gemv_rowscale(acts[(n, k)][:m], wq, ws, outs[(n, m)])
+
+    step_weight_bytes = sum((n * k + 4 * n) for (n, k) in GEMV_SHAPES for _ in GEMV_MS)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = step_weight_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"GEMV step: {ms_per_step:.4f} ms/step, {value:.1f} GB/s weight (wall {wall:.3f} s)")
+
+    # ------------------------------------------ per-call GEMV figures (events)
+    gemv_detail = []
+    for (n, k) in GEMV_SHAPES:
+        copies = weights[(n, k)]
+        for m in GEMV_MS:
+            x = acts[(n, k)][:m]
+            o = outs[(n, m)]
+            ms = time_launches(lambda i: qp.fp8_gemv_rowscale(
+                x, copies[i % len(copies)][0], copies[i % len(copies)][1], o),
+                iters=max(20, 2 * len(copies)))
+            wgbs = (n * k + 4 * n) / (ms * 1e-3) / 1e9
+            agbs = gemv_bytes(m, n, k) / (ms * 1e-3) / 1e9
+            gemv_detail.append({"n": n, "k": k, "m": m, "us": round(ms * 1e3, 2),
+                                "weight_GBs": round(wgbs, 1),
+                                "algorithmic_GBs": round(agbs, 1),
+                                "frac_hbm": round(agbs / HBM_PEAK_GBS, 4)})
+            log(f"  gemv N={n} M={m}: {ms*1e3:.2f} us  weight {wgbs:.0f} GB/s  "
+                f"({agbs / HBM_PEAK_GBS:.1%} of HBM)")
+    dom = next(d for d in gemv_detail if d["n"] == 152064 and d["m"] == 16)
+    dom_bytes = gemv_bytes(16, 152064, 5120)
+    roofline = {"bound": "hbm", "kernel": "k_fp8_gemv_rowscale<2> (N=152064, K=5120, M=16)",
+                "achieved": round(dom_bytes / (dom["us"] * 1e-6) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_bytes / (dom["us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": dom_bytes, "avg_launch_us": dom["us"],
+                "traffic": None}
+
+    rot_copies = {str(n): len(c) for (n, _), c in weights.items()}
+
+    # ------------------------------------------------- secondary rows
+    secondary = {}
+    if not args.no_secondary:
+        del weights
+        torch.cuda.empty_cache()
+        only = set(s for s in args.only.split(",") if s)
+        secondary = run_secondary(qp, synth, dev, only)
+
+    # ------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(synth)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fp8 row-scaled GEMV decode/verify: E4M3 weight "
+                               "[N,5120] + F32 row scale, BF16 acts, "
+                               "N in {6144,17408,152064} x M in {1,2,8,16}, "
+                               "one call each per step",
+                   "weight_bytes_per_step": step_weight_bytes,
+                   "rotating_weight_copies": rot_copies},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "gemv": gemv_detail,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_secondary(qp, synth, dev, only):
+    import torch
+    res = {}
+
+    def want(name):
+        return not only or name in only
+
+    def quant_item(name, nbytes, make, call):
+        """Time a streaming kernel over rotating buffer sets (>= 1 GiB)."""
+        sets = [make() for _ in range(rot_count(nbytes))]
+        torch.cuda.synchronize()
+        ms = time_launches(lambda i: call(*sets[i % len(sets)]), iters=max(20, 2 * len(sets)))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "bytes": nbytes, "GBs": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  {name}: {ms*1e3:.2f} us  {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
+        del sets
+        torch.cuda.empty_cache()
+
+    def gemm_item(name, flops, call, dtype_peak, iters=10):
+        ms = time_launches(lambda i: call(), iters=iters)
+        tf = flops / (ms * 1e-3) / 1e12
+        ent = {"us": round(ms * 1e3, 1), "flop": flops, "TFLOPs": round(tf, 1),
+               "peak_dtype": dtype_peak, "frac_peak": round(tf / PEAK_TFLOPS[dtype_peak], 4)}
+        for d in ("int8", "fp8", "fp4", "bf16"):
+            ent[f"frac_{d}"] = round(tf / PEAK_TFLOPS[d], 4)
+        res[name] = ent
+        log(f"  {name}: {ms*1e3:.1f} us  {tf:.1f} TFLOP/s ({tf / PEAK_TFLOPS[dtype_peak]:.1%} of {dtype_peak})")
+
+    # W4A8 prefill: NVFP4 weight 17408x5120 -> int8; acts 2048x5120.
+    if want("w4a8") or want("requant_a_bf16_int8") or want("requant_w_nvfp4_int8") \
+            or want("int8_gemm_blockscaled"):
+        m, n, k = 2048, 17408, 5120
+        c = synth.w4a8_prefill(dev, m, n, k)
+        wp = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        we = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        qp.quantize_bf16_nvfp4(c.w_bf16, wp, we, c.scale2)
+        w_i8 = torch.empty((n, k), dtype=torch.int8, device=dev)
+        w_s = torch.empty((n, k // 32), dtype=torch.float32, device=dev)
+        qp.requant_w_nvfp4_int8(wp, we, c.scale2, w_i8, w_s)
+        a_i8 = torch.empty((m, k), dtype=torch.int8, device=dev)
+        a_s = torch.empty((m, k // 32), dtype=torch.float32, device=dev)
+        qp.requant_a_bf16_int8(c.a_bf16, a_i8, a_s)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        del c
+        quant_item("requant_a_bf16_int8", m * k * 2 + m * k + m * (k // 32) * 4,
+                   lambda: (synth.bf16_normal((m, k), 1.0, 7, dev),
+                            torch.empty((m, k), dtype=torch.int8, device=dev),
+                            torch.empty((m, k // 32), dtype=torch.float32, device=dev)),
+                   lambda x, q, s: qp.requant_a_bf16_int8(x, q, s))
+        quant_item("requant_w_nvfp4_int8", n * k // 2 + n * k // 16 + n * k + n * (k // 32) * 4,
+                   lambda: (wp.clone(), we.clone(),
+                            torch.empty((n, k), dtype=torch.int8, device=dev),
+                            torch.empty((n, k // 32), dtype=torch.float32, device=dev)),
+                   lambda p, e, q, s: qp.requant_w_nvfp4_int8(p, e, 1.0, q, s))
+        gemm_item("int8_gemm_blockscaled", 2 * m * n * k,
+                  lambda: qp.int8_gemm_blockscaled(a_i8, w_i8, a_s, w_s, out), "int8")
+        del wp, we, w_i8, w_s, a_i8, a_s, out
+        torch.cuda.empty_cache()
+
+    # W4A4 prefill: acts 4096x17408 -> NVFP4; NVFP4 weight 5120x17408.
+    if want("w4a4") or want("quantize_bf16_nvfp4") or want("w4a4_gemm"):
+        m, n, k = 4096, 5120, 17408
+        c = synth.w4a4_prefill(dev, m, n, k)
+        ap_ = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+        wp = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        ws = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        qp.quantize_bf16_nvfp4(c.a_bf16, ap_, as_, 1.0)
+        qp.quantize_bf16_nvfp4(c.w_bf16, wp, ws, c.scale_w2)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        a_src = c.a_bf16
+        quant_item("quantize_bf16_nvfp4", m * k * 2 + m * k // 2 + m * k // 16,
+                   lambda: (a_src.clone(),
+                            torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+                            torch.empty((m, k // 16), dtype=torch.uint8, device=dev)),
+                   lambda x, p, s: qp.quantize_bf16_nvfp4(x, p, s, 1.0))
+        gemm_item("w4a4_gemm", 2 * m * n * k,
+                  lambda: qp.w4a4_gemm(ap_, as_, wp, ws, out, 1.0, c.scale_w2), "fp16")
+        del c, a_src, ap_, as_, wp, ws, out
+        torch.cuda.empty_cache()
+
+    # Block FP8 -> row-wise FP8 requant + row-wise FP8 GEMM, M = 8192.
+    if want("fp8") or want("requant_w_blockfp8_rowwise") or want("quant_rowwise_fp8") \
+            or want("fp8_gemm_rowscale"):
+        m, n, k = 8192, 12288, 5120
+        c = synth.fp8_block(dev, m, n, k)
+        quant_item("requant_w_blockfp8_rowwise", n * k + (n // 128) * (k // 128) * 4 + n * k + n * 4,
+                   lambda: (c.w_block.clone(), c.block_grid.clone(),
+                            torch.empty((n, k), dtype=torch.uint8, device=dev),
+                            torch.empty((n,), dtype=torch.float32, device=dev)),
+                   lambda w, g, q, s: qp.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w, g, q, s))
+        quant_item("quant_rowwise_fp8", m * k * 2 + m * k + m * 4,
+                   lambda: (c.a_bf16.clone(),
+                            torch.empty((m, k), dtype=torch.uint8, device=dev),
+                            torch.empty((m,), dtype=torch.float32, device=dev)),
+                   lambda x, q, s: qp.quant_rowwise_fp8(x, q, s))
+        wq = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        wsr = torch.empty((n,), dtype=torch.float32, device=dev)
+        qp.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, c.w_block, c.block_grid, wq, wsr)
+        aq = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        asr = torch.empty((m,), dtype=torch.float32, device=dev)
+        qp.quant_rowwise_fp8(c.a_bf16, aq, asr)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        gemm_item("fp8_gemm_rowscale", 2 * m * n * k,
+                  lambda: qp.fp8_gemm_rowscale(aq, asr, wq, wsr, out), "fp8")
+        del c, wq, wsr, aq, asr, out
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(synth):
+    """The CPU oracle on a bounded sample of the GEMV step: for every
+    (N, M) pair, the first N/R weight rows, with R chosen from a short probe
+    so the timed run takes about 15 s.  Reported in the headline's unit
+    (weight GB/s over the sampled rows)."""
+    import numpy as np
+    import oracle
+    oracle.lib()
+    threads = oracle.num_threads()
+
+    def run(frac):
+        tot_bytes, t = 0, 0.0
+        for sid, (n, k) in enumerate(GEMV_SHAPES):
+            rows = max(1, int(n * frac))
+            w = synth.gemv_weight_bf16(rows, k, "cpu", shape_id=sid)
+            wq, ws = oracle.quant_rowwise_fp8(synth.to_numpy_bits(w))
+            x = synth.to_numpy_bits(synth.gemv_acts_bf16(16, k, "cpu", shape_id=sid))
+            for m in GEMV_MS:
+                t0 = time.perf_counter()
+                oracle.fp8_gemv_rowscale(x[:m], wq, ws)
+                t += time.perf_counter() - t0
+                tot_bytes += rows * k + 4 * rows
+        return tot_bytes, t
+
+    probe_frac = 1.0 / 1024
+    b, t = run(probe_frac)
+    frac = min(1.0, probe_frac * 15.0 / max(t, 1e-3))
+    b, t = run(frac)
+    gbs = b / t / 1e9
+    log(f"cpu oracle: {t:.1f} s on {threads} threads, {gbs:.4f} GB/s (fraction {frac:.4f})")
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(t, 2),
+            "sample": f"every (N, M) pair of the GEMV step on the first {frac:.4%} of "
+                      f"weight rows ({b} weight bytes)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+// qp_device.hpp -- device-side codecs and small helpers shared by the
+// gfx950 kernels of libqproj.  Written for CDNA4 wave64 only.
+//
+// Formats (the documentation pages name them "E2M1" and "E4M3"; the bit
+// layouts are the OCP ones): E4M3FN with bias 7, max 448, S.1111.111 = NaN;
+// E2M1 with magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.  Rounding onto any grid
+// is to nearest with ties to the even code, saturating at the largest
+// finite magnitude, keeping the sign of a value that rounds to zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qp {
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(16))) int i32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// f32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------ E4M3
+// Encode a finite f32 to E4M3FN: RNE, |y| >= 448 saturates to 0x7E.
+// Normal range: integer round-to-nearest-even on the f32 bit pattern (keep
+// 3 mantissa bits), then re-bias the exponent 127 -> 7.  Below 2^-6 the grid
+// is uniform with step 2^-9, so RNE of y*2^9 is the code itself.
+__device__ __forceinline__ uint32_t enc_e4m3(float y)
+{
+    uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    float a = __builtin_fabsf(y);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        uint32_t ua = __float_as_uint(a);
+        code = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
+    }
+    return code | sign;
+}
+
+// Decode E4M3FN (finite codes) to f32, exactly, with the gfx950 converter.
+__device__ __forceinline__ float dec_e4m3(uint32_t byte)
+{
+    return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// ------------------------------------------------------------------ E2M1
+// Encode a finite f32 to E2M1: the code index is the number of decision
+// thresholds |y| has passed.  Thresholds sit at the midpoints 0.25, 0.75,
+// 1.25, 1.75, 2.5, 3.5, 5; a value exactly on one goes to the even code,
+// hence ">" where the lower neighbour is even and ">=" where the upper one is.
+__device__ __forceinline__ uint32_t enc_e2m1(float y)
+{
+    uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
+    float a = __builtin_fabsf(y);
+    uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) +
+                 (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                 (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+    return c | sign;
+}
+
+// E2M1 magnitude of code c (0..15) times 2, as an integer 0..12.
+__device__ __forceinline__ float dec_e2m1(uint32_t c)
+{
+    // Table packed in two 32-bit words: twice the magnitude, 4 bits each.
+    // 2*{0, .5, 1, 1.5, 2, 3, 4, 6} = {0, 1, 2, 3, 4, 6, 8, 12}.
+    uint32_t twice = (0xC8643210u >> ((c & 7u) * 4u)) & 15u;
+    float v = (float)twice * 0.5f;
+    return (c & 8u) ? -v : v;
+}
+
+// ------------------------------------------------------------------ int8
+__device__ __forceinline__ int enc_i8(float y)
+{
+    float r = __builtin_rintf(y);
+    r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// IEEE binary32 division, correctly rounded (the library is built with
+// correctly rounded f32 division; this is the one place it is relied on).
+__device__ __forceinline__ float div_rn(float x, float y) { return x / y; }
+
+// ------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = __builtin_fmaxf(v, __shfl_xor(v, off, WAVE));
+    return v;
+}
+
+// XCD-aware remap of a linear workgroup id.  Workgroups are dispatched
+// round-robin over the 8 XCDs (each with its own L2); this makes the ids an
+// XCD runs contiguous, so neighbouring tiles that share an operand panel run
+// behind the same L2.  Returns a permutation of [0, total).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t total)
+{
+    constexpr uint32_t NX = 8;
+    uint32_t per = total / NX;           // full rounds
+    uint32_t full = per * NX;
+    if (id >= full)
+        return id;                       // the ragged tail keeps its order
+    return (id % NX) * per + id / NX;
+}
+
+} // namespace qp

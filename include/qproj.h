@@ -1,0 +1,234 @@
+/*
+ * qproj.h -- C ABI of the quantized dense projection library (libqproj.so),
+ * hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the ones described on five documentation pages about an
+ * LLM inference engine's quantized projections; each declaration below cites
+ * the page (by its source file name) and the item on it.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to dense, row-major memory whose
+ *    last dimension (K) is contiguous.  BF16 is passed as uint16_t bit
+ *    patterns; E4M3 (OCP E4M3FN) and packed E2M1 as uint8_t; packed E2M1
+ *    holds element 2j in the low nibble of byte j and 2j+1 in the high one.
+ *  - The caller owns every buffer, including scratch; the library allocates
+ *    nothing, keeps no state beyond a launch counter, and never synchronises
+ *    the host.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream) and is ordered with the caller's other work
+ *    on that stream.
+ *  - Pointers must be 16-byte aligned.  Outputs must not alias inputs.
+ *    Inputs holding NaN or Inf give unspecified (but in-bounds) results.
+ *  - Each tensor must have fewer than 2^31 elements.
+ *  - All arguments are checked on the host before any HIP call; a failed
+ *    check returns a negative QP_ERR_* code and enqueues nothing.
+ *
+ * Rounding rules (the pages leave them open; this library fixes them):
+ * absmax scaling (int8: amax/127; row-wise FP8: amax/448; NVFP4 sub-block:
+ * E4M3(amax/(6*scale2))), one IEEE binary32 division of the element by the
+ * stored scale, round-to-nearest-even onto the code grid, saturation at
+ * +-127 / +-448 / +-6, the sign of a value rounding to zero kept (E4M3 0x80,
+ * E2M1 0x8), and a block whose scale is 0 encoded as scale 0 with +0 codes.
+ */
+#ifndef QPROJ_H
+#define QPROJ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define QP_OK 0
+#define QP_ERR_NULL (-1)   /* a required pointer is NULL                   */
+#define QP_ERR_SHAPE (-2)  /* a size is 0, too large, or breaks a multiple */
+#define QP_ERR_RANGE (-3)  /* GEMV M outside 1..16                          */
+#define QP_ERR_FORMAT (-4) /* unsupported weight format tag                 */
+#define QP_ERR_HIP (-5)    /* the HIP runtime rejected a launch             */
+#define QP_ERR_ALIGN (-6)  /* a pointer is not 16-byte aligned              */
+
+/* Weight format tags of an FP8 weight (dispatch_proj_rowwise.rs tests:
+ * Fp8PerRow, Fp8BlockScaled, Fp8SingleScale, Bf16, Nvfp4). */
+enum qp_weight_format {
+    QP_FP8_PER_ROW = 0,      /* E4M3 [N,K] + F32 [N]                        */
+    QP_FP8_BLOCK128 = 1,     /* E4M3 [N,K] + F32 grid [N/128, K/128]        */
+    QP_FP8_SINGLE_SCALE = 2, /* not accepted by the row-wise requant        */
+    QP_BF16 = 3,             /* not accepted by the row-wise requant        */
+    QP_NVFP4 = 4             /* not accepted by the row-wise requant        */
+};
+
+/* ------------------------------------------------------------------------
+ * Weight requant, NVFP4 -> int8 with one F32 scale per 32
+ * (gemm_dense_int8.rs, requant_w_nvfp4_int8).
+ *   w_packed [n, k/2]  packed E2M1 codes
+ *   w_e4m3   [n, k/16] E4M3 scale of each 16-element sub-block
+ *   scale2             per-tensor F32 multiplier
+ *   w_i8     [n, k]    out: int8 codes in -127..127
+ *   w_scale  [n, k/32] out: F32 scale per 32-element block
+ * Each value is dequantised as fl(e2m1 * e4m3 * scale2) (the first product is
+ * exact), two sub-blocks are re-blocked into one 32-block, and the block is
+ * quantised with s = amax/127, q = RNE(x/s).  Requires k % 32 == 0.
+ * A one-time conversion per weight (at load or on first use).
+ * ---------------------------------------------------------------------- */
+int requant_w_nvfp4_int8(const uint8_t *w_packed, const uint8_t *w_e4m3,
+                         float scale2, int8_t *w_i8, float *w_scale,
+                         uint32_t n, uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Activation requant, BF16 -> int8 with one F32 scale per 32
+ * (gemm_dense_int8.rs, int8_gemm_faith2_prefill, first launch).
+ *   a       [m, k]    BF16
+ *   a_i8    [m, k]    out: int8 codes
+ *   a_scale [m, k/32] out: F32 scale per block, amax/127
+ * Requires k % 32 == 0.
+ * ---------------------------------------------------------------------- */
+int requant_a_bf16_int8(const uint16_t *a, int8_t *a_i8, float *a_scale,
+                        uint32_t m, uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * int8 x int8 block-scaled GEMM (gemm_dense_int8.rs, int8_gemm_faith2_prefill,
+ * second launch):
+ *   C[i,j] = bf16( sum_b a_scale[i,b] * w_scale[j,b] * P_b[i,j] ),
+ *   P_b[i,j] = sum_{t in block b} a_i8[i,t] * w_i8[j,t]   (exact int32).
+ *   a_i8 [m,k], w_i8 [n,k] (both K-contiguous), a_scale [m,k/32],
+ *   w_scale [n,k/32], out [m,n] BF16.  Requires k % 32 == 0.
+ * Each P_b is formed exactly on int8 MFMA; the scale-and-add runs in F32.
+ * ---------------------------------------------------------------------- */
+int int8_gemm_blockscaled(const int8_t *a_i8, const int8_t *w_i8,
+                          const float *a_scale, const float *w_scale,
+                          uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                          void *stream);
+
+/* The two launches of the W4A8 prefill call in one: BF16 activations are
+ * requantised into caller-owned scratch (a_i8_scratch >= m*k bytes,
+ * a_scale_scratch >= m*(k/32) floats) and the GEMM above consumes them
+ * (gemm_dense_int8.rs, int8_gemm_faith2_prefill). */
+int int8_w4a8_prefill(const uint16_t *a_bf16, const int8_t *w_i8,
+                      const float *w_scale, int8_t *a_i8_scratch,
+                      float *a_scale_scratch, uint16_t *out,
+                      uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* Test export: the exact int32 partial sum of every 32-K block,
+ * p [m, n, k/32] (p[(i*n + j)*(k/32) + b] = P_b[i,j]), computed by the same
+ * MFMA tile code as int8_gemm_blockscaled.  Requires k % 32 == 0. */
+int int8_gemm_block_partials(const int8_t *a_i8, const int8_t *w_i8,
+                             int32_t *p, uint32_t m, uint32_t n, uint32_t k,
+                             void *stream);
+
+/* ------------------------------------------------------------------------
+ * BF16 -> NVFP4 quantizer (gemm_fp4.rs, quantize_bf16_to_nvfp4).
+ *   x       [rows, k]    BF16
+ *   packed  [rows, k/2]  out: packed E2M1
+ *   scale   [rows, k/16] out: E4M3 per 16-element block
+ *   scale2               per-tensor F32 (the pages launch it with 1.0 for
+ *                        activations)
+ * sb = E4M3(fl(amax / fl(6*scale2))), d = fl(e4m3(sb)*scale2),
+ * code = E2M1(fl(x/d)) (all +0 when d == 0).  Requires k % 32 == 0.
+ * ---------------------------------------------------------------------- */
+int quantize_bf16_nvfp4(const uint16_t *x, uint8_t *packed, uint8_t *scale,
+                        float scale2, uint32_t rows, uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * NVFP4 x NVFP4 GEMM (gemm_fp4.rs, w4a4_gemm / w4a4_gemm_mfast):
+ *   C[i,j] = bf16( scale_a2 * scale_w2 *
+ *                  sum_b e4m3(a_scale[i,b]) * e4m3(w_scale[j,b]) * P_b ),
+ *   P_b = sum_{t in 16-block b} e2m1(a[i,t]) * e2m1(w[j,t]).
+ *   a_packed [m,k/2], a_scale [m,k/16], w_packed [n,k/2], w_scale [n,k/16],
+ *   out [m,n] BF16.  Requires k % 32 == 0.
+ * Each block's E4M3 scale is folded into its E2M1 operands (the product is
+ * exact in FP16), so the contraction runs on FP16 MFMA with F32
+ * accumulation and the per-block scaling costs no extra pass.
+ * ---------------------------------------------------------------------- */
+int w4a4_gemm(const uint8_t *a_packed, const uint8_t *a_scale,
+              const uint8_t *w_packed, const uint8_t *w_scale, uint16_t *out,
+              float scale_a2, float scale_w2, uint32_t m, uint32_t n,
+              uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Block-scaled FP8 -> row-wise FP8 weight requant
+ * (dispatch_proj_rowwise.rs, rowwise_pair_passthrough and
+ *  requant_weight_rowwise_fp8_cached).
+ *   fmt == QP_FP8_PER_ROW: the weight already is the row-wise pair; sets
+ *       *w_res = w, *scale_res = scale and returns QP_OK with no launch and
+ *       no write to w_out / scale_out (w_out / scale_out may be NULL; n and k
+ *       are not checked).
+ *   fmt == QP_FP8_BLOCK128: w [n,k] E4M3 with an F32 grid scale
+ *       [n/128, k/128]; per row y = bf16(fl(e4m3(w)*S[i/128][t/128])), then
+ *       s = amax(y)/448, code = E4M3(fl(y/s)) into w_out [n,k] and
+ *       scale_out [n]; sets *w_res = w_out, *scale_res = scale_out.  The BF16
+ *       intermediate never touches memory (one fused pass).  Requires
+ *       n % 128 == 0 and k % 128 == 0.
+ *   any other tag: QP_ERR_FORMAT.
+ * w_res / scale_res may be NULL when the caller does not want them.
+ * ---------------------------------------------------------------------- */
+int requant_w_blockfp8_rowwise(int fmt, const uint8_t *w, const float *scale,
+                               uint8_t *w_out, float *scale_out,
+                               const uint8_t **w_res, const float **scale_res,
+                               uint32_t n, uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Row-wise FP8 quantizer (dispatch_proj_rowwise.rs, quant_rowwise_fp8; the
+ * same arithmetic as quantize_fns.rs, quantize_to_fp8).
+ *   x [rows,k] BF16 -> q [rows,k] E4M3, scale [rows] F32 = amax/448.
+ * Requires k % 16 == 0.
+ * ---------------------------------------------------------------------- */
+int quant_rowwise_fp8(const uint16_t *x, uint8_t *q, float *scale,
+                      uint32_t rows, uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Row-wise FP8 GEMM (the contraction at the end of dispatch_proj_rowwise.rs,
+ * cublas_fp8_rowwise_proj):
+ *   C[i,j] = bf16( a_scale[i] * w_scale[j] * sum_t e4m3(a[i,t]) * e4m3(w[j,t]) ).
+ *   a [m,k] E4M3, a_scale [m] F32, w [n,k] E4M3, w_scale [n] F32,
+ *   out [m,n] BF16.  Requires k % 16 == 0.  Any m is served (no padding).
+ * ---------------------------------------------------------------------- */
+int fp8_gemm_rowscale(const uint8_t *a, const float *a_scale, const uint8_t *w,
+                      const float *w_scale, uint16_t *out, uint32_t m,
+                      uint32_t n, uint32_t k, void *stream);
+
+/* The whole row-wise projection (dispatch_proj_rowwise.rs,
+ * cublas_fp8_rowwise_proj): the weight goes through
+ * requant_w_blockfp8_rowwise (passthrough when fmt == QP_FP8_PER_ROW, else
+ * requantised into w_rowwise / w_rowwise_scale, which may be NULL for the
+ * passthrough), the BF16 activations are quantised per row into caller-owned
+ * scratch (act_q >= m*k bytes, act_scale >= m floats), then
+ * fp8_gemm_rowscale writes out [m,n].  Requires k % 128 == 0 for block
+ * weights, k % 16 == 0 otherwise. */
+int fp8_rowwise_proj(int fmt, const uint8_t *w, const float *w_scale,
+                     uint8_t *w_rowwise, float *w_rowwise_scale,
+                     const uint16_t *act, uint8_t *act_q, float *act_scale,
+                     uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                     void *stream);
+
+/* ------------------------------------------------------------------------
+ * Row-scaled FP8 GEMV for decode / verify batches
+ * (fp8_gemv_batch.rs, fp8_gemv_rowscale_batch8_rt2 / _batch16_rt2,
+ *  dense_gemv_fp8w_batch2):
+ *   C[i,j] = bf16( row_scale[j] * sum_t x[i,t] * e4m3(w[j,t]) ),
+ *   x [m,k] BF16, w [n,k] E4M3, row_scale [n] F32, out [m,n] BF16.
+ * 1 <= m <= 16 (else QP_ERR_RANGE); k % 16 == 0.  The weight is streamed
+ * from memory once for all m rows, and every output row is bit-identical to
+ * the m == 1 call on that row.
+ * ---------------------------------------------------------------------- */
+int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
+                      const float *row_scale, uint16_t *out, uint32_t m,
+                      uint32_t n, uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Library information.
+ * ---------------------------------------------------------------------- */
+/* Number of kernel launches this process has enqueued through the library
+ * (a passthrough adds none). */
+uint64_t qproj_launch_count(void);
+/* Static description of a return code. */
+const char *qproj_status_string(int status);
+/* ABI version of this header. */
+int qproj_abi_version(void);
+#define QPROJ_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QPROJ_H */

@@ -22,3 +22,17 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.hookimpl(hookwrapper=True)
+def pytest_runtest_makereport(item, call):
+    # A HIP runtime error (memory fault, illegal address) poisons the device
+    # for the rest of the process: stop the whole session at the first one
+    # instead of letting later tests run on a faulted GPU.
+    outcome = yield
+    rep = outcome.get_result()
+    if rep.failed and call.excinfo is not None:
+        text = str(call.excinfo.value)
+        if "HIP error" in text or "hipError" in text or "illegal memory" in text:
+            pytest.exit(f"HIP runtime error in {item.nodeid}: {text.splitlines()[0]}",
+                        returncode=3)

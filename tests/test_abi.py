@@ -1,0 +1,129 @@
+"""C-ABI contract tests that need no GPU.
+
+The library must export every function include/qproj.h declares, and every
+argument check must happen on the host before any HIP call, so these tests
+call the entry points with bad arguments (and with fake, never dereferenced
+device addresses) and expect the documented error codes.  The row-wise
+passthrough is pure pointer logic (dispatch_proj_rowwise.rs,
+rowwise_pair_passthrough and its tests) and is checked here too, including
+that it launches nothing (the analogue of the pages' alloc_count() == 0).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gemv_nvfp4_int8_amd as qp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qproj.h")
+
+FAKE = 0x10000          # aligned, never dereferenced
+FAKE2 = 0x20000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\**\s*([a-z_0-9]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["requant_w_nvfp4_int8", "requant_a_bf16_int8", "int8_gemm_blockscaled",
+              "quantize_bf16_nvfp4", "w4a4_gemm", "requant_w_blockfp8_rowwise",
+              "fp8_gemv_rowscale", "quant_rowwise_fp8", "fp8_gemm_rowscale",
+              "int8_gemm_block_partials", "qproj_launch_count"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", qp.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, missing
+    L = qp.lib()
+    for n in _declared_functions():
+        assert hasattr(L, n)
+
+
+def test_abi_version_and_status_strings():
+    assert qp.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert qp.status_string(code) != "unknown status"
+    assert qp.status_string(-99) == "unknown status"
+
+
+L = qp.lib()
+
+
+def test_gemv_m_range_and_k_multiple():
+    for m in (0, 17, 100):
+        assert L.fp8_gemv_rowscale(FAKE, FAKE, FAKE, FAKE, m, 64, 64, None) == qp.QP_ERR_RANGE
+    assert L.fp8_gemv_rowscale(FAKE, FAKE, FAKE, FAKE, 4, 64, 40, None) == qp.QP_ERR_SHAPE
+    assert L.fp8_gemv_rowscale(FAKE, FAKE, FAKE, FAKE, 4, 0, 64, None) == qp.QP_ERR_SHAPE
+    assert L.fp8_gemv_rowscale(None, FAKE, FAKE, FAKE, 4, 64, 64, None) == qp.QP_ERR_NULL
+    assert L.fp8_gemv_rowscale(FAKE + 4, FAKE, FAKE, FAKE, 4, 64, 64, None) == qp.QP_ERR_ALIGN
+
+
+def test_int8_paths_need_k_multiple_of_32():
+    assert L.requant_a_bf16_int8(FAKE, FAKE, FAKE, 4, 48, None) == qp.QP_ERR_SHAPE
+    assert L.requant_w_nvfp4_int8(FAKE, FAKE, 1.0, FAKE, FAKE, 4, 16, None) == qp.QP_ERR_SHAPE
+    assert L.int8_gemm_blockscaled(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 80, None) == qp.QP_ERR_SHAPE
+    assert L.int8_gemm_block_partials(FAKE, FAKE, None, 4, 4, 64, None) == qp.QP_ERR_NULL
+    assert L.int8_w4a8_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 64, None) == qp.QP_ERR_SHAPE
+
+
+def test_sizes_beyond_2_pow_31_elements_are_rejected():
+    assert L.requant_a_bf16_int8(FAKE, FAKE, FAKE, 1 << 20, 1 << 12, None) == qp.QP_ERR_SHAPE
+    assert L.fp8_gemv_rowscale(FAKE, FAKE, FAKE, FAKE, 1, 1 << 20, 1 << 12, None) == qp.QP_ERR_SHAPE
+
+
+def test_nvfp4_and_rowwise_shape_rules():
+    assert L.quantize_bf16_nvfp4(FAKE, FAKE, FAKE, 1.0, 4, 16, None) == qp.QP_ERR_SHAPE
+    assert L.quantize_bf16_nvfp4(FAKE, FAKE, FAKE + 1, 1.0, 4, 64, None) == qp.QP_ERR_ALIGN
+    assert L.w4a4_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 4, 4, 48, None) == qp.QP_ERR_SHAPE
+    assert L.quant_rowwise_fp8(FAKE, FAKE, FAKE, 4, 24, None) == qp.QP_ERR_SHAPE
+    assert L.fp8_gemm_rowscale(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 8, None) == qp.QP_ERR_SHAPE
+
+
+def _requant(fmt, w, s, wo, so, n=4096, k=5120):
+    wres, sres = ctypes.c_void_p(0), ctypes.c_void_p(0)
+    st = L.requant_w_blockfp8_rowwise(fmt, w, s, wo, so, ctypes.byref(wres),
+                                      ctypes.byref(sres), n, k, None)
+    return st, wres.value, sres.value
+
+
+def test_an_already_rowwise_weight_passes_through_verbatim():
+    # The pages' fixture pointers 0xBEEF / 0x5CA1E, n = 4096, k = 5120.
+    before = qp.launch_count()
+    st, w, s = _requant(qp.QP_FP8_PER_ROW, 0xBEEF, 0x5CA1E, None, None)
+    assert st == qp.QP_OK and (w, s) == (0xBEEF, 0x5CA1E)
+    assert qp.launch_count() == before      # no launch, no write
+
+
+def test_other_formats_are_never_passed_through():
+    for fmt in (qp.QP_FP8_SINGLE_SCALE, qp.QP_BF16, qp.QP_NVFP4, 7, -1):
+        st, w, s = _requant(fmt, 0xBEEF, 0x5CA1E, FAKE, FAKE2)
+        assert st == qp.QP_ERR_FORMAT and (w, s) == (None, None)
+
+
+def test_block_format_checks_shape_before_any_launch():
+    before = qp.launch_count()
+    st, w, s = _requant(qp.QP_FP8_BLOCK128, FAKE, FAKE, FAKE2, FAKE2, n=4000, k=5120)
+    assert st == qp.QP_ERR_SHAPE and w is None
+    st, w, s = _requant(qp.QP_FP8_BLOCK128, FAKE, FAKE, None, FAKE2)
+    assert st == qp.QP_ERR_NULL
+    assert L.fp8_rowwise_proj(qp.QP_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, 4, 128, 128, None) == qp.QP_ERR_FORMAT
+    assert qp.launch_count() == before
+
+
+def test_passthrough_needs_only_the_pair():
+    st, w, s = _requant(qp.QP_FP8_PER_ROW, 0xBEEF, None, None, None)
+    assert st == qp.QP_ERR_NULL

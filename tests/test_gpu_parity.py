@@ -1,0 +1,253 @@
+"""HIP path vs the CPU oracle, element by element, at sizes the oracle
+finishes in seconds: several tiles plus ragged tails, and the edge cases of
+each format (zero blocks, saturation, exact ties, subnormal scales).
+
+Codes, scales and int32 block partials must be bit-exact; BF16 contraction
+outputs must meet the stated tolerances (tests/gpu_util.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemv_nvfp4_int8_amd as qp
+import oracle
+import synth
+from tests.gpu_util import (assert_gemm_close, assert_gemv_close, bits, dev,
+                            empty, filled, host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_rows(shape, seed, std=1.0, outliers=0.0):
+    return synth.bf16_normal(shape, std, seed, "cpu", outlier_frac=outliers,
+                             outlier_mult=20.0)
+
+
+def _with_edges(x: torch.Tensor) -> torch.Tensor:
+    """Plant edge blocks: an all-zero 32-block, a block of tiny values, a
+    block holding exact ties, a saturating spike."""
+    x = x.clone()
+    k = x.shape[1]
+    x[0, :32] = 0.0
+    if x.shape[0] > 1:
+        x[1, :32] = torch.tensor([1e-30] * 32)
+    if x.shape[0] > 2 and k >= 64:
+        t = torch.tensor([1, -2, 3, 0.25, 12, 0.75, -5, 2.5] * 4, dtype=torch.float32)
+        x[2, 32:64] = t.to(torch.bfloat16)
+    if x.shape[0] > 3:
+        x[3, k - 1] = 3.0e4
+    return x
+
+
+# ------------------------------------------------------------- quantizers
+@pytest.mark.parametrize("m,k", [(1, 32), (16, 512), (37, 160), (130, 1024)])
+def test_requant_a_bf16_int8_bit_exact(m, k):
+    a = _with_edges(_bf16_rows((m, k), 11 + m, outliers=0.01))
+    q, s = empty((m, k), torch.int8), empty((m, k // 32), torch.float32)
+    qp.requant_a_bf16_int8(dev(a), q, s)
+    oq, os_ = oracle.requant_a_bf16_int8(bits(a))
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(host(s).view(np.uint32), os_.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k,scale2", [(256, 512, 1.0), (33, 96, 0.0173), (300, 64, 2.0 ** -9)])
+def test_requant_w_nvfp4_int8_bit_exact(n, k, scale2):
+    c = synth.w4a8_tiny("cpu", m=1, n=n, k=k)
+    sc = c.w_e4m3.clone()
+    every = torch.arange(256, dtype=torch.int32)
+    every[(every & 0x7F) == 0x7F] = 0x7E               # every finite E4M3 code
+    cnt = min(256, sc.numel())
+    sc.view(-1)[:cnt] = every[:cnt].to(torch.uint8)
+    q, s = empty((n, k), torch.int8), empty((n, k // 32), torch.float32)
+    qp.requant_w_nvfp4_int8(dev(c.w_packed), dev(sc), scale2, q, s)
+    oq, os_ = oracle.requant_w_nvfp4_int8(bits(c.w_packed), bits(sc), scale2)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(host(s).view(np.uint32), os_.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,k,scale2", [(16, 512, 1.0), (33, 96, 1.0), (64, 256, None), (5, 4096, 0.37)])
+def test_quantize_bf16_nvfp4_bit_exact(rows, k, scale2):
+    x = _with_edges(_bf16_rows((rows, k), 21 + rows, std=0.02 if scale2 is None else 1.0))
+    if scale2 is None:
+        scale2 = synth.per_tensor_scale2(x)
+    p, s = empty((rows, k // 2), torch.uint8), empty((rows, k // 16), torch.uint8)
+    qp.quantize_bf16_nvfp4(dev(x), p, s, scale2)
+    op, os_ = oracle.quantize_bf16_nvfp4(bits(x), scale2)
+    assert np.array_equal(host(s), os_)
+    assert np.array_equal(host(p), op)
+
+
+@pytest.mark.parametrize("rows,k", [(1, 16), (7, 48), (40, 5120), (3, 20000), (9, 2064)])
+def test_quant_rowwise_fp8_bit_exact(rows, k):
+    x = _with_edges(_bf16_rows((rows, k), 31 + rows, std=0.02))
+    q, s = empty((rows, k), torch.uint8), empty((rows,), torch.float32)
+    qp.quant_rowwise_fp8(dev(x), q, s)
+    oq, os_ = oracle.quant_rowwise_fp8(bits(x))
+    assert np.array_equal(host(s).view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(host(q), oq)
+
+
+@pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 5120)])
+def test_requant_blockfp8_rowwise_bit_exact(n, k):
+    cse = synth.fp8_block("cpu", m=1, n=n, k=k)
+    w, grid = cse.w_block, cse.block_grid
+    wo, so = empty((n, k), torch.uint8), empty((n,), torch.float32)
+    wres, sres = qp.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, dev(w), dev(grid), wo, so)
+    assert (wres, sres) == (wo.data_ptr(), so.data_ptr())
+    oq, os_ = oracle.requant_w_blockfp8_rowwise(bits(w), grid.numpy())
+    assert np.array_equal(host(so).view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(host(wo), oq)
+
+
+def test_rowwise_weight_passes_through_without_launch_or_write():
+    n, k = 256, 512
+    w = dev(synth.uniform_bytes((n, k), 5))
+    s = dev(torch.rand(n))
+    wo, so = filled((n, k), torch.uint8), filled((n,), torch.float32)
+    before = qp.launch_count()
+    wres, sres = qp.requant_w_blockfp8_rowwise(qp.QP_FP8_PER_ROW, w, s, wo, so)
+    assert (wres, sres) == (w.data_ptr(), s.data_ptr())
+    assert qp.launch_count() == before
+    assert bool((wo == 0xA5).all()) and bool((so.view(torch.uint8) == 0xA5).all())
+
+
+# ------------------------------------------------------------ contractions
+@pytest.mark.parametrize("m,n,k", [(16, 256, 512), (130, 200, 96), (1, 129, 32)])
+def test_int8_block_partials_bit_exact(m, n, k):
+    g = torch.Generator().manual_seed(m * 1000 + n)
+    a = torch.randint(-127, 128, (m, k), generator=g, dtype=torch.int8)
+    w = torch.randint(-127, 128, (n, k), generator=g, dtype=torch.int8)
+    a[0, :32] = 127
+    w[0, :32] = 127                                        # extreme partial 516128
+    p = filled((m, n, k // 32), torch.int32)
+    qp.int8_gemm_block_partials(dev(a), dev(w), p)
+    assert np.array_equal(host(p), oracle.int8_block_partials(a.numpy(), w.numpy()))
+
+
+def test_w4a8_tiny_pipeline_matches_oracle():
+    """configs: W4A8 tiny (NVFP4 256x512 -> int8/per-32, BF16 acts 16x512)."""
+    c = synth.w4a8_tiny("cpu")
+    n, k, m = c.n, c.k, c.m
+    w_i8, w_s = empty((n, k), torch.int8), empty((n, k // 32), torch.float32)
+    a_i8, a_s = empty((m, k), torch.int8), empty((m, k // 32), torch.float32)
+    out = filled((m, n), torch.bfloat16)
+    qp.requant_w_nvfp4_int8(dev(c.w_packed), dev(c.w_e4m3), c.scale2, w_i8, w_s)
+    qp.int8_w4a8_prefill(dev(c.a_bf16), w_i8, w_s, a_i8, a_s, out)
+    ow, ows = oracle.requant_w_nvfp4_int8(bits(c.w_packed), bits(c.w_e4m3), c.scale2)
+    oa, oas = oracle.requant_a_bf16_int8(bits(c.a_bf16))
+    assert np.array_equal(host(w_i8), ow) and np.array_equal(host(w_s), ows)
+    assert np.array_equal(host(a_i8), oa) and np.array_equal(host(a_s), oas)
+    p = empty((m, n, k // 32), torch.int32)
+    qp.int8_gemm_block_partials(a_i8, w_i8, p)
+    assert np.array_equal(host(p), oracle.int8_block_partials(oa, ow))
+    assert_gemm_close(host(out), oracle.int8_gemm_blockscaled(oa, ow, oas, ows), "w4a8 tiny")
+
+
+@pytest.mark.parametrize("m,n,k", [(130, 200, 96), (256, 384, 1024), (7, 64, 5120)])
+def test_int8_gemm_blockscaled_ragged(m, n, k):
+    a = _bf16_rows((m, k), 41 + m, outliers=0.01)
+    w = _bf16_rows((n, k), 42 + n, std=0.02)
+    oa, oas = oracle.requant_a_bf16_int8(bits(a))
+    ow, ows = oracle.requant_a_bf16_int8(bits(w))
+    out = filled((m, n), torch.bfloat16)
+    qp.int8_gemm_blockscaled(dev(torch.from_numpy(oa)), dev(torch.from_numpy(ow)),
+                             dev(torch.from_numpy(oas)), dev(torch.from_numpy(ows)), out)
+    assert_gemm_close(host(out), oracle.int8_gemm_blockscaled(oa, ow, oas, ows), f"int8 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 96, 256), (33, 70, 160), (200, 300, 1024), (5, 130, 4096)])
+def test_w4a4_gemm_matches_oracle(m, n, k):
+    a = _bf16_rows((m, k), 51 + m)
+    w = _bf16_rows((n, k), 52 + n, std=0.02)
+    sw2 = synth.per_tensor_scale2(w)
+    ap, asc = oracle.quantize_bf16_nvfp4(bits(a), 1.0)
+    wp, wsc = oracle.quantize_bf16_nvfp4(bits(w), sw2)
+    out = filled((m, n), torch.bfloat16)
+    t = lambda x: dev(torch.from_numpy(x))
+    qp.w4a4_gemm(t(ap), t(asc), t(wp), t(wsc), out, 1.0, sw2)
+    assert_gemm_close(host(out), oracle.w4a4_gemm(ap, asc, wp, wsc, 1.0, sw2), f"w4a4 {m}x{n}x{k}")
+
+
+def test_w4a4_every_scale_code_and_nibble():
+    # All 16 E2M1 codes against all finite E4M3 scale codes.
+    m, n, k = 32, 128, 256
+    g = torch.Generator().manual_seed(3)
+    ap = torch.randint(0, 256, (m, k // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    wp = torch.randint(0, 256, (n, k // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    codes = torch.arange(256, dtype=torch.int32)
+    codes = codes[(codes & 0x7F) != 0x7F].to(torch.uint8)
+    asc = codes[torch.randint(0, codes.numel(), (m, k // 16), generator=g)]
+    wsc = codes[torch.randint(0, codes.numel(), (n, k // 16), generator=g)]
+    out = filled((m, n), torch.bfloat16)
+    qp.w4a4_gemm(dev(ap), dev(asc), dev(wp), dev(wsc), out, 1.0, 1.0)
+    ref = oracle.w4a4_gemm(ap.numpy(), asc.numpy(), wp.numpy(), wsc.numpy(), 1.0, 1.0)
+    assert_gemm_close(host(out), ref, "w4a4 all codes")
+
+
+@pytest.mark.parametrize("m,n,k", [(130, 200, 272), (256, 384, 1024), (3, 70, 5120)])
+def test_fp8_gemm_rowscale_matches_oracle(m, n, k):
+    a = _bf16_rows((m, k), 61 + m)
+    w = _bf16_rows((n, k), 62 + n, std=0.02)
+    oa, oas = oracle.quant_rowwise_fp8(bits(a))
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    out = filled((m, n), torch.bfloat16)
+    t = lambda x: dev(torch.from_numpy(x))
+    qp.fp8_gemm_rowscale(t(oa), t(oas), t(ow), t(ows), out)
+    assert_gemm_close(host(out), oracle.fp8_gemm_rowscale(oa, oas, ow, ows), f"fp8 {m}x{n}x{k}")
+
+
+def test_fp8_rowwise_proj_block_and_passthrough():
+    m, n, k = 70, 256, 512
+    cse = synth.fp8_block("cpu", m=m, n=n, k=k)
+    t = lambda x: dev(torch.from_numpy(x))
+    # block-scaled layer: requant + activation quant + GEMM in one call
+    wr, wrs = empty((n, k), torch.uint8), empty((n,), torch.float32)
+    aq, asc = empty((m, k), torch.uint8), empty((m,), torch.float32)
+    out = filled((m, n), torch.bfloat16)
+    qp.fp8_rowwise_proj(qp.QP_FP8_BLOCK128, dev(cse.w_block), dev(cse.block_grid),
+                        wr, wrs, dev(cse.a_bf16), aq, asc, out)
+    ow, ows = oracle.requant_w_blockfp8_rowwise(bits(cse.w_block), cse.block_grid.numpy())
+    oa, oas = oracle.quant_rowwise_fp8(bits(cse.a_bf16))
+    assert np.array_equal(host(wr), ow) and np.array_equal(host(aq), oa)
+    assert_gemm_close(host(out), oracle.fp8_gemm_rowscale(oa, oas, ow, ows), "proj block")
+    # already row-wise layer: passthrough, no requant launch
+    pw, pws = oracle.quant_rowwise_fp8(bits(cse.w_rowwise_bf16))
+    out2 = filled((m, n), torch.bfloat16)
+    before = qp.launch_count()
+    qp.fp8_rowwise_proj(qp.QP_FP8_PER_ROW, t(pw), t(pws), None, None,
+                        dev(cse.a_bf16), aq, asc, out2)
+    assert qp.launch_count() - before == 2            # act quant + GEMM only
+    assert_gemm_close(host(out2), oracle.fp8_gemm_rowscale(oa, oas, pw, pws), "proj rowwise")
+
+
+@pytest.mark.parametrize("n,k", [(37, 512), (200, 48), (6144, 5120)])
+def test_fp8_gemv_rowscale_all_m(n, k):
+    w = synth.gemv_weight_bf16(n, k, "cpu")
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    wq, ws = dev(torch.from_numpy(ow)), dev(torch.from_numpy(ows))
+    x = synth.gemv_acts_bf16(16, k, "cpu")
+    for m in range(1, 17):
+        out = filled((m, n), torch.bfloat16)
+        qp.fp8_gemv_rowscale(dev(x[:m].contiguous()), wq, ws, out)
+        assert_gemv_close(host(out), oracle.fp8_gemv_rowscale(bits(x[:m]), ow, ows), f"gemv m={m}")
+
+
+@pytest.mark.parametrize("n,k", [(300, 512), (17408, 5120)])
+def test_fp8_gemv_batched_rows_bit_identical_to_single_row(n, k):
+    """The pages' invariant for the batched GEMV (fp8_gemv_batch.rs,
+    dense_gemv_fp8w_batch2): each row of an M-row call equals, bit for bit,
+    an M = 1 call on that row."""
+    w = synth.gemv_weight_bf16(n, k, "cpu", shape_id=1)
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    wq, ws = dev(torch.from_numpy(ow)), dev(torch.from_numpy(ows))
+    x = dev(synth.gemv_acts_bf16(16, k, "cpu", shape_id=1))
+    singles = []
+    for i in range(16):
+        o = empty((1, n), torch.bfloat16)
+        qp.fp8_gemv_rowscale(x[i:i + 1], wq, ws, o)
+        singles.append(o)
+    single = torch.cat(singles)
+    for m in (2, 8, 16):
+        o = empty((m, n), torch.bfloat16)
+        qp.fp8_gemv_rowscale(x[:m], wq, ws, o)
+        assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
