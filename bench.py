@@ -54,7 +54,29 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="GEMV step only")
     ap.add_argument("--only", default="", help="comma list of secondary items to run")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="for hardware-counter runs: one plain 1 GiB copy (counter "
+                         "calibration), then the lm_head GEMV at each M, 5 launches each")
     return ap.parse_args()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (two rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a
+    1 GiB copy); None when the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "fp8_gemv_lm_head_hbm_traffic.md")
+    try:
+        fields = dict(l.split(": ", 1) for l in open(path).read().splitlines()
+                      if l.startswith(("traffic_bytes_per_launch:", "kernel_source:",
+                                       "kernel_source_sha256_16:")))
+        src = os.path.join(ROOT, fields["kernel_source"].strip())
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if h != fields["kernel_source_sha256_16"].strip():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def gemv_bytes(m, n, k):
@@ -96,6 +118,9 @@ def main():
 
     dev = torch.device("cuda:0")
     qp.lib()
+    if args.roofline_only:
+        roofline_only(qp, synth, dev)
+        return
 
     # ---------------------------------------------------------- GEMV setup
     log("setting up GEMV weights")
@@ -159,14 +184,17 @@ def main():
                                 "frac_hbm": round(agbs / HBM_PEAK_GBS, 4)})
             log(f"  gemv N={n} M={m}: {ms*1e3:.2f} us  weight {wgbs:.0f} GB/s  "
                 f"({agbs / HBM_PEAK_GBS:.1%} of HBM)")
-    dom = next(d for d in gemv_detail if d["n"] == 152064 and d["m"] == 16)
-    dom_bytes = gemv_bytes(16, 152064, 5120)
-    roofline = {"bound": "hbm", "kernel": "k_fp8_gemv_rowscale<2> (N=152064, K=5120, M=16)",
-                "achieved": round(dom_bytes / (dom["us"] * 1e-6) / 1e9, 1),
+    # Dominant kernel: the lm_head GEMV (N=152064) over the step's M mix.
+    dom = [d for d in gemv_detail if d["n"] == 152064]
+    dom_bytes = sum(gemv_bytes(d["m"], 152064, 5120) for d in dom) / len(dom)
+    dom_us = sum(d["us"] for d in dom) / len(dom)
+    roofline = {"bound": "hbm",
+                "kernel": "k_fp8_gemv_rows<2,1> (N=152064, K=5120, M in {1,2,8,16})",
+                "achieved": round(dom_bytes / (dom_us * 1e-6) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom_bytes / (dom["us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "bytes_per_launch": dom_bytes, "avg_launch_us": dom["us"],
-                "traffic": None}
+                "frac": round(dom_bytes / (dom_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes_per_launch": round(dom_bytes), "avg_launch_us": round(dom_us, 2),
+                "traffic": measured_traffic()}
 
     rot_copies = {str(n): len(c) for (n, _), c in weights.items()}
 
@@ -208,6 +236,35 @@ def main():
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
+
+
+def roofline_only(qp, synth, dev):
+    """A short program for counter runs: a device-to-device copy of exactly
+    1 GiB (reads 1 GiB, writes 1 GiB: the scale for FETCH_SIZE / WRITE_SIZE),
+    then 5 launches of the lm_head GEMV at each M, each on a fresh weight copy
+    (two copies of 778 MB, so nothing stays cache-resident)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    n, k = 152064, 5120
+    wb = synth.gemv_weight_bf16(n, k, dev, shape_id=2)
+    wq = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty((n,), dtype=torch.float32, device=dev)
+    qp.quant_rowwise_fp8(wb, wq, ws)
+    del wb
+    copies = [(wq, ws), (wq.clone(), ws.clone())]
+    x = synth.gemv_acts_bf16(16, k, dev, shape_id=2)
+    i = 0
+    for m in GEMV_MS:
+        o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        for _ in range(5):
+            qp.fp8_gemv_rowscale(x[:m], copies[i % 2][0], copies[i % 2][1], o)
+            i += 1
+    torch.cuda.synchronize()
+    log("roofline-only run done")
 
 
 def run_secondary(qp, synth, dev, only):

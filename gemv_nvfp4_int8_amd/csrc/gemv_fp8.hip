@@ -7,18 +7,22 @@
 // Design (MI355X-first):
 //  * The contraction runs on MFMA, not on the vector ALU: at 8 TB/s an M=16
 //    GEMV needs ~250 TFLOP/s, beyond the FP32 vector peak.  The E4M3 weight
-//    converts exactly to BF16 (v_cvt_scalef32_pk_bf16_fp8, scale 1.0), the
-//    activations already are BF16, and v_mfma_f32_16x16x32_bf16 forms exact
-//    products with F32 accumulation.  The activation rows are the MFMA's 16
-//    M-rows; rows >= M are zero and cost nothing in memory.
-//  * Each weight byte is loaded once, with 16-byte loads straight into the
-//    MFMA B-operand registers (no LDS for the weight).  A K-range that a
-//    lane owns is the same in the A and B operands, so the MFMA's K order is
-//    free to follow memory order.
-//  * One 256-thread workgroup owns 16*T weight rows; its four waves split K
-//    into interleaved 64-element steps and their partial tiles are added in
-//    a fixed order through LDS.  Nothing in the reduction depends on M, so
-//    every output row is bit-identical to an M = 1 call on that row.
+//    converts exactly to BF16 (v_cvt_scalef32_pk_bf16_fp8 with a unit scale),
+//    the activations already are BF16, and v_mfma_f32_16x16x32_bf16 forms
+//    exact products with F32 accumulation.  The activation rows are the
+//    MFMA's 16 M-rows, so one pass over the weight serves every row; rows
+//    >= M are zero and cost no memory traffic.
+//  * The weight is read once, with 64-lane loads that each cover 4 rows x
+//    256 contiguous bytes: HBM3E serves such bursts at ~6.9 TB/s on this
+//    part, against ~5 TB/s for the 16 rows x 64 bytes an MFMA-shaped load
+//    would touch.  Each wave transposes its bytes through a private LDS tile
+//    into MFMA operand layout.
+//  * Two work splits, chosen from N alone (see gemv_wide): wide weights give
+//    each wave its own rows over all of K, with the activation segment staged
+//    once per workgroup in LDS and shared by its four waves; narrow weights
+//    split K over the four waves of a workgroup (everything wave-private) and
+//    add the partial tiles in a fixed order.  No summation order depends on
+//    M, so every output row is bit-identical to an M = 1 call on that row.
 #include "qp_device.hpp"
 #include "qp_launch.hpp"
 
@@ -44,77 +48,258 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v)
     return __builtin_bit_cast(bf16x8, v);
 }
 
-constexpr int GEMV_WAVES = 4;      // K-split ways inside a workgroup
-constexpr int GEMV_STEP = 64;      // K elements per wave step (4 lanes x 16)
-constexpr int GEMV_UNROLL = 4;     // steps in flight per wave
+// ---------------------------------------------------------------------------
+// Wide weights: each wave owns 16*T rows over all of K; the four waves walk K
+// together in 256-element segments.  Per segment:
+//   * the weight bytes are loaded with every 64-lane instruction covering 4
+//     rows x 256 contiguous bytes (HBM serves such bursts far better than the
+//     16 rows x 64 bytes an MFMA-shaped load would touch), written to a
+//     wave-private LDS tile and read back in MFMA operand layout;
+//   * the activation segment [16 x 256] BF16 is loaded once per workgroup
+//     into LDS (double-buffered, one barrier per segment) and shared by the
+//     four waves.
+// Loads run D segments ahead of the MFMAs.
+// ---------------------------------------------------------------------------
+constexpr int GV_SEG = 256;                 // K elements per segment
+constexpr int GV_WPITCH = GV_SEG + 16;      // LDS bytes per weight row
+constexpr int GV_XPITCH = GV_SEG + 8;       // LDS bf16 per activation row
 
 template <int T>
-__global__ __launch_bounds__(256) void k_fp8_gemv_rowscale(
+struct GvSeg {
+    u32x4 w[4 * T];     // 4T instructions of 4 rows x 256 B
+    u32x4 x[2];         // 2 x 16 B of the workgroup's activation segment
+};
+
+template <int T, int D>
+__global__ __launch_bounds__(256) void k_fp8_gemv_rows(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
     const float *__restrict__ rs, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k)
 {
-    __shared__ f32x4 red[GEMV_WAVES - 1][T][WAVE];
+    constexpr int ROWS = 16 * T;
+    __shared__ __attribute__((aligned(16))) uint8_t sw[4][ROWS * GV_WPITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sx[2][16 * GV_XPITCH];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int col = lane & 15;     // MFMA row of A (activation) and column of B (weight row)
-    const int grp = lane >> 4;     // which 16-element slice of a 64-element step
-    const uint32_t n0 = blockIdx.x * (16u * T);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const uint32_t row0 = blockIdx.x * (4 * ROWS) + wave * ROWS;
+    const uint32_t nseg = (k + GV_SEG - 1) / GV_SEG;
 
-    const uint8_t *wrow[T];
-    bool wok[T];
+    // Weight loads: instruction j covers rows row0 + 4j .. + 3, lane -> row
+    // 4j + grp, bytes 16*col of the segment.  Rows past n re-read row n-1.
+    const uint8_t *wsrc[4 * T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        uint32_t nn = n0 + 16u * t + col;
-        wok[t] = nn < n;
-        wrow[t] = w + (size_t)(wok[t] ? nn : 0u) * k;
+    for (int j = 0; j < 4 * T; ++j) {
+        uint32_t r = row0 + 4 * j + grp;
+        wsrc[j] = w + (size_t)(r < n ? r : n - 1) * k + 16 * col;
     }
-    const bool xok = (uint32_t)col < m;
-    const uint16_t *xrow = x + (size_t)(xok ? col : 0) * k;
+    // Activation loads: 16 rows x 256 bf16 = 512 chunks of 16 B, two per
+    // thread: chunk c = tid + 256 i -> row c / 32, element 8 * (c % 32).
+    const uint16_t *xsrc[2];
+    bool xrow_ok[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        int c = tid + 256 * i, r = c >> 5;
+        xrow_ok[i] = (uint32_t)r < m;
+        xsrc[i] = x + (size_t)(xrow_ok[i] ? r : 0) * k + 8 * (c & 31);
+    }
+
+    auto load = [&](GvSeg<T> &g, uint32_t seg) {
+        uint32_t kb = seg * GV_SEG;
+        bool full = kb + GV_SEG <= k;
+#pragma unroll
+        for (int j = 0; j < 4 * T; ++j) {
+            uint32_t kk = kb + 16 * col;
+            g.w[j] = (u32x4){0, 0, 0, 0};
+            if (full || kk < k)
+                g.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wsrc[j] + kb));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int c = tid + 256 * i;
+            uint32_t kk = kb + 8 * (c & 31);
+            g.x[i] = (u32x4){0, 0, 0, 0};
+            if (xrow_ok[i] && (full || kk < k))
+                g.x[i] = *reinterpret_cast<const u32x4 *>(xsrc[i] + kb);
+        }
+    };
+    auto stash = [&](const GvSeg<T> &g, int buf) {
+#pragma unroll
+        for (int j = 0; j < 4 * T; ++j)
+            *reinterpret_cast<u32x4 *>(&sw[wave][(4 * j + grp) * GV_WPITCH + 16 * col]) = g.w[j];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int c = tid + 256 * i;
+            *reinterpret_cast<u32x4 *>(&sx[buf][(c >> 5) * GV_XPITCH + 8 * (c & 31)]) = g.x[i];
+        }
+    };
 
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t)
         acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    const uint32_t nsteps = (k + GEMV_STEP - 1) / GEMV_STEP;
-    for (uint32_t s0 = wave; s0 < nsteps; s0 += GEMV_WAVES * GEMV_UNROLL) {
-        u32x4 wv[GEMV_UNROLL][T];
-        u32x4 xa[GEMV_UNROLL], xb[GEMV_UNROLL];
+    GvSeg<T> g[D];
 #pragma unroll
-        for (int u = 0; u < GEMV_UNROLL; ++u) {
-            uint32_t s = s0 + GEMV_WAVES * u;
-            uint32_t kk = s * GEMV_STEP + 16u * grp;
-            bool kok = s < nsteps && kk < k;
+    for (int d = 0; d < D; ++d)
+        if ((uint32_t)d < nseg)
+            load(g[d], d);
+
+    for (uint32_t seg = 0; seg < nseg; ++seg) {
+        const int buf = seg & 1;
+        GvSeg<T> &cur = g[0];
+        stash(cur, buf);
+        // rotate the prefetch queue and refill its tail
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                wv[u][t] = (u32x4){0, 0, 0, 0};
-                if (kok && wok[t])
-                    wv[u][t] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(wrow[t] + kk));
-            }
-            xa[u] = (u32x4){0, 0, 0, 0};
-            xb[u] = (u32x4){0, 0, 0, 0};
-            if (kok && xok) {
-                const u32x4 *xp = reinterpret_cast<const u32x4 *>(xrow + kk);
-                xa[u] = xp[0];
-                xb[u] = xp[1];
-            }
-        }
+        for (int d = 0; d + 1 < D; ++d)
+            g[d] = g[d + 1];
+        if (seg + D < nseg)
+            load(g[D - 1], seg + D);
+        __syncthreads();
 #pragma unroll
-        for (int u = 0; u < GEMV_UNROLL; ++u) {
+        for (int u = 0; u < GV_SEG / 64; ++u) {
+            // lane (col, grp): activation row col, k = 64u + 16 grp .. +15
+            const uint16_t *xp = &sx[buf][col * GV_XPITCH + 64 * u + 16 * grp];
+            u32x4 xa = *reinterpret_cast<const u32x4 *>(xp);
+            u32x4 xb = *reinterpret_cast<const u32x4 *>(xp + 8);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
+                u32x4 wv = *reinterpret_cast<const u32x4 *>(
+                    &sw[wave][(16 * t + col) * GV_WPITCH + 64 * u + 16 * grp]);
                 bf16x8 blo, bhi;
-                fp8x16_to_bf16(wv[u][t], blo, bhi);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u]), blo, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[u]), bhi, acc[t], 0, 0, 0);
+                fp8x16_to_bf16(wv, blo, bhi);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
             }
         }
     }
 
-    // Fixed-order reduction of the four K-partial tiles.
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        uint32_t nn = row0 + 16u * t + col;
+        if (nn < n) {
+            float sc = rs[nn];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t mm = 4u * grp + i;
+                if (mm < m)
+                    out[(size_t)mm * n + nn] = (uint16_t)f32_to_bf16(acc[t][i] * sc);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Narrow weights: too few rows to give every CU several workgroups, so the
+// four waves of a workgroup share 16*T rows and split K into contiguous
+// quarters.  Everything is wave-private (the weight transpose tile and the
+// activation segment live in the wave's own LDS region, so the loop has no
+// barrier), D segments are loaded ahead, and the four partial tiles are
+// added in a fixed order at the end.
+// ---------------------------------------------------------------------------
+template <int T>
+struct GvSegW {
+    u32x4 w[4 * T];
+    u32x4 x[8];          // 16 rows x 256 bf16 = 512 chunks of 16 B, 8 per lane
+};
+
+template <int T, int D>
+__global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
+    const float *__restrict__ rs, uint16_t *__restrict__ out,
+    uint32_t m, uint32_t n, uint32_t k)
+{
+    constexpr int ROWS = 16 * T;
+    __shared__ __attribute__((aligned(16))) uint8_t sw[4][ROWS * GV_WPITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sx[4][16 * GV_XPITCH];
+    __shared__ f32x4 red[3][T][WAVE];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const uint32_t row0 = blockIdx.x * ROWS;
+    const uint32_t nseg = (k + GV_SEG - 1) / GV_SEG;
+    const uint32_t per = (nseg + 3) / 4;
+    const uint32_t s_beg = min(nseg, per * wave), s_end = min(nseg, s_beg + per);
+
+    const uint8_t *wsrc[4 * T];
+#pragma unroll
+    for (int j = 0; j < 4 * T; ++j) {
+        uint32_t r = row0 + 4 * j + grp;
+        wsrc[j] = w + (size_t)(r < n ? r : n - 1) * k + 16 * col;
+    }
+    // activation chunk c = lane + 64 i: row c / 32, element 8 * (c % 32)
+    const uint16_t *xsrc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int c = lane + 64 * i, r = c >> 5;
+        xsrc[i] = x + (size_t)((uint32_t)r < m ? r : 0) * k + 8 * (c & 31);
+    }
+
+    auto load = [&](GvSegW<T> &g, uint32_t seg) {
+        uint32_t kb = seg * GV_SEG;
+        bool full = kb + GV_SEG <= k;
+#pragma unroll
+        for (int j = 0; j < 4 * T; ++j) {
+            g.w[j] = (u32x4){0, 0, 0, 0};
+            if (full || kb + 16 * col < k)
+                g.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wsrc[j] + kb));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int c = lane + 64 * i;
+            g.x[i] = (u32x4){0, 0, 0, 0};
+            if ((uint32_t)(c >> 5) < m && (full || kb + 8 * (c & 31) < k))
+                g.x[i] = *reinterpret_cast<const u32x4 *>(xsrc[i] + kb);
+        }
+    };
+    auto stash = [&](const GvSegW<T> &g) {
+#pragma unroll
+        for (int j = 0; j < 4 * T; ++j)
+            *reinterpret_cast<u32x4 *>(&sw[wave][(4 * j + grp) * GV_WPITCH + 16 * col]) = g.w[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int c = lane + 64 * i;
+            *reinterpret_cast<u32x4 *>(&sx[wave][(c >> 5) * GV_XPITCH + 8 * (c & 31)]) = g.x[i];
+        }
+    };
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    GvSegW<T> g[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (s_beg + d < s_end)
+            load(g[d], s_beg + d);
+
+    for (uint32_t seg = s_beg; seg < s_end; ++seg) {
+        stash(g[0]);
+#pragma unroll
+        for (int d = 0; d + 1 < D; ++d)
+            g[d] = g[d + 1];
+        if (seg + D < s_end)
+            load(g[D - 1], seg + D);
+#pragma unroll
+        for (int u = 0; u < GV_SEG / 64; ++u) {
+            const uint16_t *xp = &sx[wave][col * GV_XPITCH + 64 * u + 16 * grp];
+            u32x4 xa = *reinterpret_cast<const u32x4 *>(xp);
+            u32x4 xb = *reinterpret_cast<const u32x4 *>(xp + 8);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                u32x4 wv = *reinterpret_cast<const u32x4 *>(
+                    &sw[wave][(16 * t + col) * GV_WPITCH + 64 * u + 16 * grp]);
+                bf16x8 blo, bhi;
+                fp8x16_to_bf16(wv, blo, bhi);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
+            }
+        }
+    }
+
+    // Fixed-order reduction of the four K-quarter partial tiles.
     if (wave > 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
@@ -125,39 +310,58 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rowscale(
         return;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        f32x4 r = acc[t];
 #pragma unroll
-        for (int v = 0; v < GEMV_WAVES - 1; ++v)
-            r += red[v][t][lane];
-        // lane holds rows 4*grp + i (i = 0..3) of column `col`
-        uint32_t nn = n0 + 16u * t + col;
+        for (int v = 0; v < 3; ++v)
+            acc[t] += red[v][t][lane];
+        uint32_t nn = row0 + 16u * t + col;
         if (nn < n) {
             float sc = rs[nn];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t mm = 4u * grp + i;
                 if (mm < m)
-                    out[(size_t)mm * n + nn] = (uint16_t)f32_to_bf16(r[i] * sc);
+                    out[(size_t)mm * n + nn] = (uint16_t)f32_to_bf16(acc[t][i] * sc);
             }
         }
     }
 }
 
+template <int T, int D>
+static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float *rs,
+                               uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                               hipStream_t st)
+{
+    constexpr uint32_t rows_wg = 16 * T;
+    uint32_t grid = (n + rows_wg - 1) / rows_wg;
+    hipLaunchKernelGGL((k_fp8_gemv_ksplit<T, D>), dim3(grid), dim3(256), 0, st,
+                       x, w, rs, out, m, n, k);
+}
+
+template <int T, int D>
+static void launch_gemv_rows(const uint16_t *x, const uint8_t *w, const float *rs,
+                             uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                             hipStream_t st)
+{
+    constexpr uint32_t rows_wg = 64 * T;
+    uint32_t grid = (n + rows_wg - 1) / rows_wg;
+    hipLaunchKernelGGL((k_fp8_gemv_rows<T, D>), dim3(grid), dim3(256), 0, st,
+                       x, w, rs, out, m, n, k);
+}
+
+// Work-split choice: it depends on n only (never on m), which keeps every
+// row's summation order, and so its bits, the same for every m.  Wide
+// weights (lm_head-class) give every CU several row-split workgroups; narrow
+// ones split K inside the workgroup to keep enough waves streaming.
+static bool gemv_wide(uint32_t n) { return n >= 65536u; }
+
 hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
                                     const float *rs, uint16_t *out, uint32_t m,
                                     uint32_t n, uint32_t k, hipStream_t st)
 {
-    // Two 16-row tiles per workgroup when there are enough rows to keep all
-    // 256 CUs busy; one otherwise.  Depends on n only (never on m).
-    if (n >= 32u * 1024u) {
-        uint32_t grid = (n + 31) / 32;
-        hipLaunchKernelGGL(k_fp8_gemv_rowscale<2>, dim3(grid), dim3(256), 0, st,
-                           x, w, rs, out, m, n, k);
-    } else {
-        uint32_t grid = (n + 15) / 16;
-        hipLaunchKernelGGL(k_fp8_gemv_rowscale<1>, dim3(grid), dim3(256), 0, st,
-                           x, w, rs, out, m, n, k);
-    }
+    if (gemv_wide(n))
+        launch_gemv_rows<2, 1>(x, w, rs, out, m, n, k, st);
+    else
+        launch_gemv_ksplit<1, 1>(x, w, rs, out, m, n, k, st);
     count_launch();
     return hipGetLastError();
 }

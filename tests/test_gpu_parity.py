@@ -251,3 +251,17 @@ def test_fp8_gemv_batched_rows_bit_identical_to_single_row(n, k):
         o = empty((m, n), torch.bfloat16)
         qp.fp8_gemv_rowscale(x[:m], wq, ws, o)
         assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
+
+
+@pytest.mark.parametrize("n,k", [(70000, 512), (65552, 1040), (37, 1040)])
+def test_fp8_gemv_wide_and_partial_segments(n, k):
+    # n >= 65536 takes the row-split kernel; k = 1040 ends 16 elements into a
+    # 256-element segment; n = 70000 / 65552 leave ragged row tiles.
+    w = synth.gemv_weight_bf16(n, k, "cpu", shape_id=2)
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    wq, ws = dev(torch.from_numpy(ow)), dev(torch.from_numpy(ows))
+    x = synth.gemv_acts_bf16(16, k, "cpu", shape_id=2)
+    for m in (1, 3, 16):
+        out = filled((m, n), torch.bfloat16)
+        qp.fp8_gemv_rowscale(dev(x[:m].contiguous()), wq, ws, out)
+        assert_gemv_close(host(out), oracle.fp8_gemv_rowscale(bits(x[:m]), ow, ows), f"gemv {n}x{k} m={m}")
