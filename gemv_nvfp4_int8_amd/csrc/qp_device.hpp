@@ -83,7 +83,7 @@ __device__ __forceinline__ uint32_t enc_e2m1(float y)
     return c | sign;
 }
 
-// E2M1 magnitude of code c (0..15) times 2, as an integer 0..12.
+// E2M1 value of code c (0..15).
 __device__ __forceinline__ float dec_e2m1(uint32_t c)
 {
     // Table packed in two 32-bit words: twice the magnitude, 4 bits each.
@@ -102,8 +102,93 @@ __device__ __forceinline__ int enc_i8(float y)
 }
 
 // IEEE binary32 division, correctly rounded (the library is built with
-// correctly rounded f32 division; this is the one place it is relied on).
+// correctly rounded f32 division).
 __device__ __forceinline__ float div_rn(float x, float y) { return x / y; }
+
+// Correctly rounded x / s for many x and one s, in three operations per x.
+// With r = RN(1/s) (one IEEE division per scale), q0 = RN(x*r) is within an
+// ulp of x/s, the remainder x - q0*s is exact in one FMA, and
+// RN(q0 + rem*r) is RN(x/s) (Markstein's correction theorem: a reciprocal
+// within half an ulp and a quotient within one ulp give the correctly
+// rounded quotient, barring underflow and overflow).  The correction loses
+// the sign of a zero quotient (-0/s would come out +0), and RN(x/s) always
+// has the sign of q0, so q0's sign bit is copied onto the result.  Scales
+// outside [2^-100, 2^100] fall back to the division instruction sequence.
+struct ScaleDiv {
+    float s, r;
+    bool fast;
+    __device__ __forceinline__ explicit ScaleDiv(float s_) : s(s_)
+    {
+        fast = s_ >= 0x1p-100f && s_ <= 0x1p100f;
+        r = fast ? div_rn(1.0f, s_) : 0.0f;
+    }
+    __device__ __forceinline__ float operator()(float x) const
+    {
+        if (fast) {
+            float q0 = x * r;
+            float rem = __builtin_fmaf(-q0, s, x);
+            float q = __builtin_fmaf(rem, r, q0);
+            return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) |
+                                   (__float_as_uint(q0) & 0x80000000u));
+        }
+        return div_rn(x, s);
+    }
+};
+
+// Hardware converters.  Each was compared on this part with the software
+// encoders above over every binary32 input of its domain (both signs) and
+// agrees bit for bit: E4M3 for |y| <= 448 (beyond 464 the converter returns
+// NaN, so inputs are clamped to +-448 first, which RNE maps to 448 anyway),
+// E2M1 for |y| <= 8 (inputs are clamped to +-6), BF16 for every finite y.
+__device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b)
+{
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four E4M3 codes of (a, b, c, d) in one dword, a in the low byte.
+__device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d)
+{
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Eight E2M1 codes of v[0..7] in one dword, v[0] in the low nibble.
+__device__ __forceinline__ uint32_t cvt_e2m1x8(const float *v)
+{
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        c[i] = __builtin_amdgcn_fmed3f(v[i], -6.0f, 6.0f);
+    uint32_t o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, c[0], c[1], 1.0f, 0);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, c[2], c[3], 1.0f, 1);
+    o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, c[4], c[5], 1.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, c[6], c[7], 1.0f, 3);
+}
+
+// Four int8 codes RNE(v[i]) for |v| < 127.5, v[0] in the low byte: rounded
+// to an integer, biased by 128 (exact) and packed by the u8 converter, then
+// un-biased with one XOR.
+__device__ __forceinline__ uint32_t cvt_i8x4(const float *v)
+{
+    uint32_t o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[0]) + 128.0f, 0, 0u);
+    o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[1]) + 128.0f, 1, o);
+    o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[2]) + 128.0f, 2, o);
+    o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[3]) + 128.0f, 3, o);
+    return o ^ 0x80808080u;
+}
+
+// The two E2M1 values of byte SEL of w (low nibble first), exactly.
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1_pair(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
 
 // ------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float v)

@@ -44,11 +44,14 @@ __global__ __launch_bounds__(256) void k_requant_a_bf16_int8(
     float sc = div_rn(amax, 127.0f);
     u32x4 out = {0, 0, 0, 0};
     if (sc != 0.0f) {
+        ScaleDiv d(sc);
+        float t[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t b = (uint32_t)enc_i8(div_rn(x[i], sc)) & 0xFFu;
-            out[i / 4] |= b << (8 * (i % 4));
-        }
+        for (int i = 0; i < 16; ++i)
+            t[i] = d(x[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            out[j] = cvt_i8x4(&t[4 * j]);
     }
     if (valid) {
         *reinterpret_cast<u32x4 *>(q + (size_t)c * 16) = out;
@@ -88,11 +91,16 @@ __global__ __launch_bounds__(256) void k_requant_w_nvfp4_int8(
     float d0 = dec_e4m3(scw & 0xFFu), d1 = dec_e4m3(scw >> 8);
     float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        uint32_t byte = (p[i / 8] >> (8 * ((i / 2) % 4))) & 0xFFu;
-        uint32_t code = (i % 2 == 0) ? (byte & 15u) : (byte >> 4);
-        float prod = dec_e2m1(code) * (i < 16 ? d0 : d1);   // exact
-        v[i] = prod * scale2;
+    for (int w = 0; w < 4; ++w) {
+        // E2M1 pairs of the four bytes of word w (low nibble = even element)
+        f32x2 e[4] = {e2m1_pair<0>(p[w]), e2m1_pair<1>(p[w]), e2m1_pair<2>(p[w]),
+                      e2m1_pair<3>(p[w])};
+        float dd = w < 2 ? d0 : d1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[8 * w + 2 * j] = (e[j][0] * dd) * scale2;      // e2m1*e4m3 is exact
+            v[8 * w + 2 * j + 1] = (e[j][1] * dd) * scale2;
+        }
     }
     float amax = 0.0f;
 #pragma unroll
@@ -101,10 +109,14 @@ __global__ __launch_bounds__(256) void k_requant_w_nvfp4_int8(
     float sc = div_rn(amax, 127.0f);
     u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
     if (sc != 0.0f) {
+        ScaleDiv d(sc);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            o0[i / 4] |= ((uint32_t)enc_i8(div_rn(v[i], sc)) & 0xFFu) << (8 * (i % 4));
-            o1[i / 4] |= ((uint32_t)enc_i8(div_rn(v[16 + i], sc)) & 0xFFu) << (8 * (i % 4));
+        for (int i = 0; i < 32; ++i)
+            v[i] = d(v[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o0[j] = cvt_i8x4(&v[4 * j]);
+            o1[j] = cvt_i8x4(&v[16 + 4 * j]);
         }
     }
     u32x4 *qo = reinterpret_cast<u32x4 *>(q + (size_t)b * 32);
@@ -162,11 +174,12 @@ __global__ __launch_bounds__(256) void k_quantize_bf16_nvfp4(
         float d = dec_e4m3(sb) * scale2;
         scales |= sb << (8 * blk);
         if (d != 0.0f) {
+            ScaleDiv dv(d);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint32_t code = enc_e2m1(div_rn(v[i], d));
-                out[2 * blk + i / 8] |= code << (4 * (i % 8));
-            }
+            for (int i = 0; i < 16; ++i)
+                v[i] = dv(v[i]);
+            out[2 * blk] = cvt_e2m1x8(&v[0]);
+            out[2 * blk + 1] = cvt_e2m1x8(&v[8]);
         }
     }
     *reinterpret_cast<u32x4 *>(packed + (size_t)c * 16) = out;
@@ -198,15 +211,18 @@ __device__ __forceinline__ float block_max_256(float v, float *red)
                            __builtin_fmaxf(red[2], red[3]));
 }
 
-// Encode 8 f32 values (already divided-by-scale inputs are formed here) to
-// E4M3 bytes packed in two dwords.
-__device__ __forceinline__ u32x2 enc8_e4m3(const float *v, float sc)
+// E4M3 codes of v[0..7] / sc (correctly rounded quotients) in two dwords;
+// all +0 when the scale is 0.
+__device__ __forceinline__ u32x2 enc8_e4m3(const float *v, const ScaleDiv &d, bool zero)
 {
     u32x2 o = {0, 0};
-    if (sc != 0.0f) {
+    if (!zero) {
+        float t[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            o[i / 4] |= enc_e4m3(div_rn(v[i], sc)) << (8 * (i % 4));
+            t[i] = d(v[i]);
+        o[0] = cvt_e4m3x4(t[0], t[1], t[2], t[3]);
+        o[1] = cvt_e4m3x4(t[4], t[5], t[6], t[7]);
     }
     return o;
 }
@@ -238,6 +254,7 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8(
     }
     amax = block_max_256(amax, red);
     const float sc = div_rn(amax, 448.0f);
+    const ScaleDiv dv(sc);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         uint32_t c = threadIdx.x + 256u * j;
@@ -248,7 +265,7 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8(
                 v[2 * i] = bf16_lo(raw[j][i]);
                 v[2 * i + 1] = bf16_hi(raw[j][i]);
             }
-            *reinterpret_cast<u32x2 *>(q + (size_t)row * k + (size_t)c * 8) = enc8_e4m3(v, sc);
+            *reinterpret_cast<u32x2 *>(q + (size_t)row * k + (size_t)c * 8) = enc8_e4m3(v, dv, sc == 0.0f);
         }
     }
     if (threadIdx.x == 0)
@@ -274,6 +291,7 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8_long(
     }
     amax = block_max_256(amax, red);
     const float sc = div_rn(amax, 448.0f);
+    const ScaleDiv dv(sc);
     for (uint32_t c = threadIdx.x; c < nch; c += 256) {
         u32x4 r = *reinterpret_cast<const u32x4 *>(xr + (size_t)c * 8);
         float v[8];
@@ -282,7 +300,7 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8_long(
             v[2 * i] = bf16_lo(r[i]);
             v[2 * i + 1] = bf16_hi(r[i]);
         }
-        *reinterpret_cast<u32x2 *>(q + (size_t)row * k + (size_t)c * 8) = enc8_e4m3(v, sc);
+        *reinterpret_cast<u32x2 *>(q + (size_t)row * k + (size_t)c * 8) = enc8_e4m3(v, dv, sc == 0.0f);
     }
     if (threadIdx.x == 0)
         s[row] = sc;
@@ -315,12 +333,22 @@ hipError_t launch_quant_rowwise_fp8(const uint16_t *x, uint8_t *q, float *s,
 // intermediate y = bf16(fl(e4m3(w)*S)) is formed in registers, never stored.
 // CPT 16-byte chunks (16 codes each, inside one 128-column block) per thread.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void bf16_pair(f32x2 e, float scale, float *y)
+{
+    // times the block scale (one f32 rounding), then to BF16 (RNE), back to f32
+    bf16x2 b = (bf16x2){(__bf16)(e[0] * scale), (__bf16)(e[1] * scale)};
+    uint32_t bits = __builtin_bit_cast(uint32_t, b);
+    y[0] = bf16_lo(bits);
+    y[1] = bf16_hi(bits);
+}
+
 __device__ __forceinline__ void blockfp8_to_bf16_vals(u32x4 raw, float scale, float *y)
 {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float p = dec_e4m3((raw[i / 4] >> (8 * (i % 4))) & 0xFFu) * scale;
-        y[i] = __uint_as_float(f32_to_bf16(p) << 16);
+    for (int w = 0; w < 4; ++w) {
+        // two E4M3 codes per converter call, exactly
+        bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false), scale, &y[4 * w]);
+        bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true), scale, &y[4 * w + 2]);
     }
 }
 
@@ -352,11 +380,12 @@ __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise(
     }
     amax = block_max_256(amax, red);
     const float sc = div_rn(amax, 448.0f);
+    const ScaleDiv dv(sc);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         uint32_t c = threadIdx.x + 256u * j;
         if (c < nch) {
-            u32x2 lo = enc8_e4m3(&y[j][0], sc), hi = enc8_e4m3(&y[j][8], sc);
+            u32x2 lo = enc8_e4m3(&y[j][0], dv, sc == 0.0f), hi = enc8_e4m3(&y[j][8], dv, sc == 0.0f);
             u32x4 o = {lo[0], lo[1], hi[0], hi[1]};
             *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = o;
         }
@@ -385,10 +414,11 @@ __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_long(
     }
     amax = block_max_256(amax, red);
     const float sc = div_rn(amax, 448.0f);
+    const ScaleDiv dv(sc);
     for (uint32_t c = threadIdx.x; c < nch; c += 256) {
         u32x4 raw = *reinterpret_cast<const u32x4 *>(wr + (size_t)c * 16);
         blockfp8_to_bf16_vals(raw, gr[(c * 16) / 128], y);
-        u32x2 lo = enc8_e4m3(&y[0], sc), hi = enc8_e4m3(&y[8], sc);
+        u32x2 lo = enc8_e4m3(&y[0], dv, sc == 0.0f), hi = enc8_e4m3(&y[8], dv, sc == 0.0f);
         u32x4 o = {lo[0], lo[1], hi[0], hi[1]};
         *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = o;
     }

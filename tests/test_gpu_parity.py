@@ -36,6 +36,9 @@ def _with_edges(x: torch.Tensor) -> torch.Tensor:
         x[2, 32:64] = t.to(torch.bfloat16)
     if x.shape[0] > 3:
         x[3, k - 1] = 3.0e4
+    # signed zeros and tiny negatives keep their sign through every encoder
+    x[-1, 1::7] = -0.0
+    x[-1, 3::11] = -1e-30
     return x
 
 
@@ -90,7 +93,9 @@ def test_quant_rowwise_fp8_bit_exact(rows, k):
 @pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 5120)])
 def test_requant_blockfp8_rowwise_bit_exact(n, k):
     cse = synth.fp8_block("cpu", m=1, n=n, k=k)
-    w, grid = cse.w_block, cse.block_grid
+    w, grid = cse.w_block.clone(), cse.block_grid
+    w[1, ::5] = 0x80                     # -0.0 codes
+    w[2, ::3] = 0x81                     # smallest negative subnormal
     wo, so = empty((n, k), torch.uint8), empty((n,), torch.float32)
     wres, sres = qp.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, dev(w), dev(grid), wo, so)
     assert (wres, sres) == (wo.data_ptr(), so.data_ptr())
