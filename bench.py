@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="GEMV step only")
     ap.add_argument("--only", default="", help="comma list of secondary items to run")
+    ap.add_argument("--skip-gemv", action="store_true",
+                    help="run only the secondary rows (for profiling them); prints "
+                         "their JSON dictionary instead of the headline line")
     ap.add_argument("--roofline-only", action="store_true",
                     help="for hardware-counter runs: one plain 1 GiB copy (counter "
                          "calibration), then the lm_head GEMV at each M, 5 launches each")
@@ -120,6 +123,10 @@ def main():
     qp.lib()
     if args.roofline_only:
         roofline_only(qp, synth, dev)
+        return
+    if args.skip_gemv:
+        only = set(s for s in args.only.split(",") if s)
+        print(json.dumps({"secondary": run_secondary(qp, synth, dev, only)}), flush=True)
         return
 
     # ---------------------------------------------------------- GEMV setup

@@ -10,6 +10,8 @@
 #include "gemm_common.hpp"
 #include "qp_launch.hpp"
 
+#include <type_traits>
+
 namespace qp {
 
 constexpr int F8_BM = 128, F8_BN = 128, F8_BK = 128;
@@ -104,14 +106,285 @@ __global__ __launch_bounds__(256) void k_fp8_gemm_rowscale(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Large-tile variant for K % 128 == 0 and M, N >= 256: 256 x 256 workgroup
+// tiles, each wave a 128 x 128 block of 4 x 4 MFMA tiles (accumulators in
+// AGPRs).  K advances in stages of 128 bytes (two MFMA steps).  Operand
+// panels (256 rows x 128 bytes = 32 KB of A or of W) are DMA'd into a ring
+// of five LDS slots, all 160 KB of the CU: while a stage computes from two
+// slots, the other three hold loads in flight 1 to 2 stages ahead, enough
+// to cover L2 and HBM latency at the rate the MFMAs consume data (32 bytes
+// per clock per CU).  Panel i of the sequence A0, W0, A1, W1, ... lives in
+// slot i % 5.
+//
+// The last tile row / column is shifted back to end at M / N, so every row a
+// tile loads exists (no clamping: DMA addresses stay affine in the
+// instruction index) and the rows / columns it shares with its neighbour are
+// not stored twice.
+//
+// The MFMAs compute C^T tiles (W fragment as the first operand): lane l then
+// holds row l % 32 of C and, in accumulator registers 4q .. 4q+3, four
+// consecutive columns 8q + 4*(l/32) .. +3, so the epilogue scales and
+// converts four outputs at a time and writes them with one 8-byte store.
+// The MFMA is issued with zero scale operands, which selects the unscaled
+// encoding (identical results to unit E8M0 scales, at lower power).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
+    const uint8_t *__restrict__ A, const float *__restrict__ as,
+    const uint8_t *__restrict__ W, const float *__restrict__ ws,
+    uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
+    uint32_t mtiles, uint32_t ntiles, uint32_t vec_ok)
+{
+    // The five slots are separate LDS variables: accesses to distinct
+    // variables carry distinct alias scopes, so the compiler can see that
+    // reading one slot need not wait for the DMA into another (with one
+    // array it would wait for every DMA in flight).
+    __shared__ __attribute__((aligned(1024))) uint8_t S0[BIG_ROWS * BIG_KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t S1[BIG_ROWS * BIG_KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t S2[BIG_ROWS * BIG_KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t S3[BIG_ROWS * BIG_KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t S4[BIG_ROWS * BIG_KB];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t nst = K / BIG_KB;
+
+    uint32_t tm, tn;
+    tile_coords(mtiles, ntiles, tm, tn);
+    const uint32_t m0 = tm * 256, n0 = tn * 256;
+    const uint32_t m0e = min(m0, M - 256), n0e = min(n0, N - 256);
+    const uint8_t *const a_rows = A + (size_t)(m0e + 64 * wave) * K;
+    const uint8_t *const w_rows = W + (size_t)(n0e + 64 * wave) * K;
+
+    // DMA of one panel (the layout of dma_stage): instruction j of wave w
+    // fills kilobyte 8w+j = rows 64w + 8j + lane/8; lane's physical chunk
+    // lane%8 holds logical chunk (lane%8) ^ swz(row) with swz(row) =
+    // ((j & 1) << 2) | (lane >> 4).  The lane part of the source offset
+    // therefore takes two values (even / odd j); the rest is uniform.
+    uint32_t dvo[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        dvo[e] = (uint32_t)(lane >> 3) * K + 16u * ((lane & 7) ^ ((e << 2) | (lane >> 4)));
+    // Panel of stage st; stages past the end reload the last one (in bounds,
+    // never read) so that every stage issues the same loads.
+    auto dma_panel = [&](const uint8_t *rows, uint32_t st, uint8_t *slot) {
+        const uint8_t *src = rows + (st < nst ? st : nst - 1) * BIG_KB;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds(src + (size_t)(8 * j) * K + dvo[j & 1],
+                                             (lds_void *)(slot + 1024 * (8 * wave + j)), 16, 0, 0);
+    };
+
+    // LDS fragment reads: tile row wm*128 + 32t + lane%32 of a slot, logical
+    // chunk c at physical c ^ (((lane%32) >> 1) & 7).  The lane part of the
+    // address depends on c only; t and the wave's half are immediate or
+    // uniform offsets.
+    const int g = lane >> 5;
+    uint32_t lrow[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int lc = (c >> 1) * 4 + 2 * g + (c & 1);         // chunks 2g, 2g+1, 4+2g, 5+2g
+        lrow[c] = (lane & 31) * BIG_KB + 16 * (lc ^ (((lane & 31) >> 1) & 7));
+    }
+    // Lane offsets for the current stage.  They are re-derived once per
+    // stage (an empty asm hides their value; it is placed ahead of all of
+    // the stage's memory operations, which it orders), so each read costs
+    // one add instead of one register per slot and offset held across the
+    // whole loop.
+    uint32_t lo[4];
+    auto launder = [&]() {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            lo[c] = lrow[c];
+        asm volatile("" : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]));
+    };
+    struct Frags {
+        i32x8 a[4], w[4];
+    };
+    auto read_frags = [&](Frags &f, const uint8_t *la, const uint8_t *lw, int ks) {
+        const uint32_t o0 = lo[2 * ks], o1 = lo[2 * ks + 1];
+        const uint8_t *pa0 = la + wm * 128 * BIG_KB + o0, *pa1 = la + wm * 128 * BIG_KB + o1;
+        const uint8_t *pw0 = lw + wn * 128 * BIG_KB + o0, *pw1 = lw + wn * 128 * BIG_KB + o1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            u32x4 a0 = *reinterpret_cast<const u32x4 *>(pa0 + 32 * BIG_KB * t);
+            u32x4 a1 = *reinterpret_cast<const u32x4 *>(pa1 + 32 * BIG_KB * t);
+            u32x4 w0 = *reinterpret_cast<const u32x4 *>(pw0 + 32 * BIG_KB * t);
+            u32x4 w1 = *reinterpret_cast<const u32x4 *>(pw1 + 32 * BIG_KB * t);
+            f.a[t] = (i32x8){(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            f.w[t] = (i32x8){(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
+                             (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+        }
+    };
+    // acc[ti][tj]: C^T block of A tile ti (32 rows of C) and W tile tj
+    f32x16 acc[4][4];
+    // MFMAs [lo, hi) of the 16 (4 x 4 tiles) of one K step
+    auto mfma_range = [&](const Frags &f, int lo_, int hi_) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (i >= lo_ && i < hi_)
+                acc[i / 4][i % 4] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.w[i % 4], f.a[i / 4], acc[i / 4][i % 4], 0, 0, 0, 0, 0, 0);
+    };
+    auto interleave = [&](int n_mfma, int n_ds, int n_vmem) {
+        // n_ds LDS reads and n_vmem DMA loads, two after each of the first
+        // MFMAs (reads early, so they have returned by the time their
+        // fragments are needed)
+        for (int i = 0; i < n_mfma; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (2 * i < n_ds)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if (2 * i < n_vmem)
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        }
+    };
+    // Wait until at most n of this wave's loads are in flight and its LDS
+    // reads have returned, then for every wave.  Hard scheduling fences
+    // keep the MFMAs on their side of it.
+    auto sync_stage = [&](auto n) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(decltype(n)::value));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Stage st, X = (st, K step 0) already in registers, A(st) and W(st) in
+    // slots ca and cw, A(st+1) and W(st+1) due in na and nw:
+    //   16 MFMAs on X + LDS reads of Y = (st, K step 1)
+    //    4 MFMAs on Y
+    //   sync: A(st+1) and W(st+1) have landed (only A(st+2) may still be
+    //         in flight: 8 loads per wave), and every wave has finished
+    //         reading ca and cw
+    //   DMA of W(st+2) into ca and A(st+3) into cw
+    //   12 MFMAs on Y + LDS reads of X = (st+1, K step 0) and the DMA,
+    //      all issued over the first 8, so the reads have returned before
+    //      the next stage needs them
+    // The slots are passed as the LDS variables themselves so that every
+    // access names its slot statically.
+    Frags X, Y;
+    constexpr int Y_PRE = 4;      // MFMAs on Y before the sync
+    auto stage = [&](uint32_t st, uint8_t *ca, uint8_t *cw, const uint8_t *na,
+                     const uint8_t *nw) {
+        launder();
+        read_frags(Y, ca, cw, 1);
+        mfma_range(X, 0, 16);
+        interleave(16, 16, 0);
+        mfma_range(Y, 0, Y_PRE);
+        sync_stage(std::integral_constant<int, 8>());
+        dma_panel(w_rows, st + 2, ca);
+        dma_panel(a_rows, st + 3, cw);
+        read_frags(X, na, nw, 0);
+        mfma_range(Y, Y_PRE, 16);
+        interleave(16 - Y_PRE, 16, 16);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+    dma_panel(a_rows, 0, S0);
+    dma_panel(w_rows, 0, S1);
+    dma_panel(a_rows, 1, S2);
+    dma_panel(w_rows, 1, S3);
+    dma_panel(a_rows, 2, S4);
+    sync_stage(std::integral_constant<int, 24>());
+    launder();
+    read_frags(X, S0, S1, 0);
+    uint32_t st = 0;
+    for (; st + 5 <= nst; st += 5) {
+        stage(st + 0, S0, S1, S2, S3);
+        stage(st + 1, S2, S3, S4, S0);
+        stage(st + 2, S4, S0, S1, S2);
+        stage(st + 3, S1, S2, S3, S4);
+        stage(st + 4, S3, S4, S0, S1);
+    }
+    if (st < nst)
+        stage(st + 0, S0, S1, S2, S3);
+    if (st + 1 < nst)
+        stage(st + 1, S2, S3, S4, S0);
+    if (st + 2 < nst)
+        stage(st + 2, S4, S0, S1, S2);
+    if (st + 3 < nst)
+        stage(st + 3, S1, S2, S3, S4);
+    // the loads past the end must land before the workgroup's LDS is freed
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+    // Epilogue: C[i][j] = bf16(acc * (as[i] * ws[j])).  Lane rows
+    // i = ib + 32*ti, columns j = jb + 32*tj + 8*q + c (c = 0..3); a shifted
+    // tile stores only rows >= m0 and columns >= n0.
+    const uint32_t ib = m0e + wm * 128 + (lane & 31);
+    const uint32_t jb = n0e + wn * 128 + 4 * (lane >> 5);
+    if (vec_ok && m0e == m0 && n0e == n0) {
+        float sa[4];
+        f32x4 sw[4][4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+            sa[ti] = as[ib + 32 * ti];
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sw[tj][q] = *reinterpret_cast<const f32x4 *>(ws + jb + 32 * tj + 8 * q);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            uint16_t *orow = out + (size_t)(ib + 32 * ti) * N + jb;
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x16 &c = acc[ti][tj];
+                    u32x2 pk;
+                    pk[0] = pk_bf16(c[4 * q + 0] * (sa[ti] * sw[tj][q][0]),
+                                    c[4 * q + 1] * (sa[ti] * sw[tj][q][1]));
+                    pk[1] = pk_bf16(c[4 * q + 2] * (sa[ti] * sw[tj][q][2]),
+                                    c[4 * q + 3] * (sa[ti] * sw[tj][q][3]));
+                    *reinterpret_cast<u32x2 *>(orow + 32 * tj + 8 * q) = pk;
+                }
+        }
+    } else {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            const uint32_t gi = ib + 32 * ti;
+            const float sai = as[gi];
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t gj = jb + 32 * tj + 8 * (r >> 2) + (r & 3);
+                    if (gi >= m0 && gj >= n0)
+                        out[(size_t)gi * N + gj] =
+                            (uint16_t)f32_to_bf16(acc[ti][tj][r] * (sai * ws[gj]));
+                }
+        }
+    }
+}
+
 hipError_t launch_fp8_gemm_rowscale(const uint8_t *a, const float *as,
                                     const uint8_t *w, const float *ws,
                                     uint16_t *out, uint32_t m, uint32_t n,
                                     uint32_t k, hipStream_t st)
 {
-    uint32_t mt = (m + F8_BM - 1) / F8_BM, nt = (n + F8_BN - 1) / F8_BN;
-    hipLaunchKernelGGL(k_fp8_gemm_rowscale, dim3(mt * nt), dim3(256), 0, st,
-                       a, as, w, ws, out, m, n, k, mt, nt);
+    if (k % BIG_KB == 0 && m >= 256 && n >= 256) {
+        uint32_t mt = (m + 255) / 256, nt = (n + 255) / 256;
+        // 8-byte output stores and 16-byte column-scale loads need N % 4 == 0
+        // and aligned base pointers; otherwise every tile takes the
+        // element-wise epilogue.
+        uint32_t vec_ok = n % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0 &&
+                          reinterpret_cast<uintptr_t>(ws) % 16 == 0;
+        hipLaunchKernelGGL(k_fp8_gemm_rowscale_big, dim3(mt * nt), dim3(256), 0, st,
+                           a, as, w, ws, out, m, n, k, mt, nt, vec_ok);
+    } else {
+        uint32_t mt = (m + F8_BM - 1) / F8_BM, nt = (n + F8_BN - 1) / F8_BN;
+        hipLaunchKernelGGL(k_fp8_gemm_rowscale, dim3(mt * nt), dim3(256), 0, st,
+                           a, as, w, ws, out, m, n, k, mt, nt);
+    }
     count_launch();
     return hipGetLastError();
 }

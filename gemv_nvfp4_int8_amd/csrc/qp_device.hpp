@@ -147,6 +147,14 @@ __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// BF16 bits of (a, b), a in the low half, by the packed converter (round to
+// nearest even; the same bits as f32_to_bf16 for every finite input).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    bf16x2 v = (bf16x2){(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Four E4M3 codes of (a, b, c, d) in one dword, a in the low byte.
 __device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d)
 {

@@ -189,7 +189,13 @@ def test_w4a4_every_scale_code_and_nibble():
     assert_gemm_close(host(out), ref, "w4a4 all codes")
 
 
-@pytest.mark.parametrize("m,n,k", [(130, 200, 272), (256, 384, 1024), (3, 70, 5120)])
+# Shapes cover both kernels: the 128 x 128 one (small M or N, K % 128 != 0)
+# and the 256 x 256 one (M, N >= 256, K % 128 == 0) with a whole number of
+# its 5-stage unroll (K = 640), a tail of 1 and of 2 stages (K = 128, 896),
+# last tiles shifted back (M = 300, 260; N = 520, 514) and N % 4 != 0 (514:
+# element-wise epilogue everywhere).
+@pytest.mark.parametrize("m,n,k", [(130, 200, 272), (256, 384, 1024), (3, 70, 5120), (300, 520, 640),
+                                   (512, 256, 128), (260, 514, 896)])
 def test_fp8_gemm_rowscale_matches_oracle(m, n, k):
     a = _bf16_rows((m, k), 61 + m)
     w = _bf16_rows((n, k), 62 + n, std=0.02)
