@@ -10,62 +10,78 @@
 namespace qp {
 
 // ---------------------------------------------------------------------------
-// BF16 -> int8, one F32 scale per 32 (gemm_dense_int8.rs,
-// int8_gemm_faith2_prefill, activation launch).  Two lanes per 32-block,
-// 16 elements per lane; the pair exchanges its partial absmax with one
-// shuffle.  Flattened indexing is valid because k % 32 == 0: a block never
-// straddles a row, and block id = chunk id / 2 in the [m, k/32] scale grid.
+// Access pattern of the elementwise kernels: a thread owns one 16-byte input
+// chunk per round, and the 64 lanes of a wave own 64 consecutive chunks, so
+// every load and store instruction covers one contiguous window (HBM serves
+// that about 1.5x faster than lanes walking their own 64-byte strips).  The
+// few lanes that share a scaling block combine their absmax with shuffles.
+// Each workgroup runs QR rounds of 256 chunks with all loads issued first
+// (QR per kernel as measured best on MI355X at the benchmark sizes: 1 for
+// the small activation requant, 2 for the others).
 // ---------------------------------------------------------------------------
+
+// ---------------------------------------------------------------------------
+// BF16 -> int8, one F32 scale per 32 (gemm_dense_int8.rs,
+// int8_gemm_faith2_prefill, activation launch).  A 32-block is 4 chunks of
+// 8 elements, held by 4 adjacent lanes.  Flattened indexing is valid because
+// k % 32 == 0: a block never straddles a row, and block id = chunk id / 4 in
+// the [m, k/32] scale grid.
+// ---------------------------------------------------------------------------
+template <int QR>
 __global__ __launch_bounds__(256) void k_requant_a_bf16_int8(
     const uint16_t *__restrict__ a, int8_t *__restrict__ q,
     float *__restrict__ s, uint32_t nchunks)
 {
-    uint32_t c = blockIdx.x * 256u + threadIdx.x;
-    bool valid = c < nchunks;            // nchunks is even: pairs agree
-    u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-    if (valid) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(a + (size_t)c * 16);
-        v0 = __builtin_nontemporal_load(p);
-        v1 = __builtin_nontemporal_load(p + 1);
+    const uint32_t base = blockIdx.x * (256u * QR) + threadIdx.x;
+    u32x4 raw[QR];
+#pragma unroll
+    for (int u = 0; u < QR; ++u) {
+        const uint32_t c = base + 256u * u;
+        raw[u] = (u32x4){0, 0, 0, 0};
+        if (c < nchunks)
+            raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a + (size_t)c * 8));
     }
-    float x[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(v0[i]);
-        x[2 * i + 1] = bf16_hi(v0[i]);
-        x[8 + 2 * i] = bf16_lo(v1[i]);
-        x[8 + 2 * i + 1] = bf16_hi(v1[i]);
-    }
-    float amax = 0.0f;
+    for (int u = 0; u < QR; ++u) {
+        const uint32_t c = base + 256u * u;     // nchunks % 4 == 0: a block's lanes agree
+        float x[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, WAVE));
-    float sc = div_rn(amax, 127.0f);
-    u32x4 out = {0, 0, 0, 0};
-    if (sc != 0.0f) {
-        ScaleDiv d(sc);
-        float t[16];
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(raw[u][i]);
+            x[2 * i + 1] = bf16_hi(raw[u][i]);
+        }
+        float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            t[i] = d(x[i]);
+        for (int i = 0; i < 8; ++i)
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, WAVE));
+        const float sc = div_rn(amax, 127.0f);
+        u32x2 out = {0, 0};
+        if (sc != 0.0f) {
+            ScaleDiv d(sc);
+            float t[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            out[j] = cvt_i8x4(&t[4 * j]);
-    }
-    if (valid) {
-        *reinterpret_cast<u32x4 *>(q + (size_t)c * 16) = out;
-        if ((c & 1u) == 0u)
-            s[c >> 1] = sc;
+            for (int i = 0; i < 8; ++i)
+                t[i] = d(x[i]);
+            out[0] = cvt_i8x4(&t[0]);
+            out[1] = cvt_i8x4(&t[4]);
+        }
+        if (c < nchunks) {
+            *reinterpret_cast<u32x2 *>(q + (size_t)c * 8) = out;
+            if ((c & 3u) == 0u)
+                s[c >> 2] = sc;
+        }
     }
 }
 
 hipError_t launch_requant_a_bf16_int8(const uint16_t *a, int8_t *q, float *s,
                                       uint32_t m, uint32_t k, hipStream_t st)
 {
-    uint32_t nchunks = (uint32_t)((uint64_t)m * k / 16);
-    uint32_t grid = (nchunks + 255) / 256;
-    hipLaunchKernelGGL(k_requant_a_bf16_int8, dim3(grid), dim3(256), 0, st,
+    uint32_t nchunks = (uint32_t)((uint64_t)m * k / 8);
+    constexpr int QR = 1;
+    uint32_t grid = (nchunks + 256 * QR - 1) / (256 * QR);
+    hipLaunchKernelGGL(k_requant_a_bf16_int8<QR>, dim3(grid), dim3(256), 0, st,
                        a, q, s, nchunks);
     count_launch();
     return hipGetLastError();
@@ -73,132 +89,161 @@ hipError_t launch_requant_a_bf16_int8(const uint16_t *a, int8_t *q, float *s,
 
 // ---------------------------------------------------------------------------
 // NVFP4 -> int8 weight requant (gemm_dense_int8.rs, requant_w_nvfp4_int8).
-// One lane per 32-block: 16 packed bytes + 2 E4M3 sub-block scales in, 32
-// int8 + 1 F32 out.  v = fl(fl(e2m1*e4m3)*scale2) (the first product exact),
-// then absmax / 127 and RNE(v/s).
+// A 32-block (16 packed bytes + 2 E4M3 sub-block scales in, 32 int8 + 1 F32
+// out) is held by two adjacent lanes, one 16-element sub-block each: 8
+// packed bytes and one scale byte in, 16 int8 out.  v = fl(fl(e2m1*e4m3) *
+// scale2) (the first product exact), then absmax / 127 and RNE(v/s).
 // ---------------------------------------------------------------------------
+template <int QR>
 __global__ __launch_bounds__(256) void k_requant_w_nvfp4_int8(
     const uint8_t *__restrict__ packed, const uint8_t *__restrict__ sc16,
     float scale2, int8_t *__restrict__ q, float *__restrict__ s,
-    uint32_t nblocks)
+    uint32_t nhalves)
 {
-    uint32_t b = blockIdx.x * 256u + threadIdx.x;
-    if (b >= nblocks)
-        return;
-    u32x4 p = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(packed + (size_t)b * 16));
-    uint32_t scw = *reinterpret_cast<const uint16_t *>(sc16 + (size_t)b * 2);
-    float d0 = dec_e4m3(scw & 0xFFu), d1 = dec_e4m3(scw >> 8);
-    float v[32];
+    const uint32_t base = blockIdx.x * (256u * QR) + threadIdx.x;
+    u32x2 p[QR];
+    uint32_t scb[QR];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        // E2M1 pairs of the four bytes of word w (low nibble = even element)
-        f32x2 e[4] = {e2m1_pair<0>(p[w]), e2m1_pair<1>(p[w]), e2m1_pair<2>(p[w]),
-                      e2m1_pair<3>(p[w])};
-        float dd = w < 2 ? d0 : d1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[8 * w + 2 * j] = (e[j][0] * dd) * scale2;      // e2m1*e4m3 is exact
-            v[8 * w + 2 * j + 1] = (e[j][1] * dd) * scale2;
+    for (int u = 0; u < QR; ++u) {
+        const uint32_t h = base + 256u * u;
+        p[u] = (u32x2){0, 0};
+        scb[u] = 0;
+        if (h < nhalves) {
+            p[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(packed + (size_t)h * 8));
+            scb[u] = sc16[h];
         }
     }
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    float sc = div_rn(amax, 127.0f);
-    u32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
-    if (sc != 0.0f) {
-        ScaleDiv d(sc);
+    for (int u = 0; u < QR; ++u) {
+        const uint32_t h = base + 256u * u;     // nhalves is even: a block's lanes agree
+        const float dd = dec_e4m3(scb[u]);
+        float v[16];
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-            v[i] = d(v[i]);
+        for (int w = 0; w < 2; ++w) {
+            // E2M1 pairs of the four bytes of word w (low nibble = even element)
+            f32x2 e[4] = {e2m1_pair<0>(p[u][w]), e2m1_pair<1>(p[u][w]), e2m1_pair<2>(p[u][w]),
+                          e2m1_pair<3>(p[u][w])};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            o0[j] = cvt_i8x4(&v[4 * j]);
-            o1[j] = cvt_i8x4(&v[16 + 4 * j]);
+            for (int j = 0; j < 4; ++j) {
+                v[8 * w + 2 * j] = (e[j][0] * dd) * scale2;      // e2m1*e4m3 is exact
+                v[8 * w + 2 * j + 1] = (e[j][1] * dd) * scale2;
+            }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+        const float sc = div_rn(amax, 127.0f);
+        u32x4 o = {0, 0, 0, 0};
+        if (sc != 0.0f) {
+            ScaleDiv d(sc);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = d(v[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = cvt_i8x4(&v[4 * j]);
+        }
+        if (h < nhalves) {
+            *reinterpret_cast<u32x4 *>(q + (size_t)h * 16) = o;
+            if ((h & 1u) == 0u)
+                s[h >> 1] = sc;
         }
     }
-    u32x4 *qo = reinterpret_cast<u32x4 *>(q + (size_t)b * 32);
-    qo[0] = o0;
-    qo[1] = o1;
-    s[b] = sc;
 }
 
 hipError_t launch_requant_w_nvfp4_int8(const uint8_t *packed, const uint8_t *sc16,
                                        float scale2, int8_t *q, float *s,
                                        uint32_t n, uint32_t k, hipStream_t st)
 {
-    uint32_t nblocks = (uint32_t)((uint64_t)n * (k / 32));
-    hipLaunchKernelGGL(k_requant_w_nvfp4_int8, dim3((nblocks + 255) / 256),
-                       dim3(256), 0, st, packed, sc16, scale2, q, s, nblocks);
+    uint32_t nhalves = (uint32_t)((uint64_t)n * (k / 16));
+    constexpr int QR = 2;
+    hipLaunchKernelGGL(k_requant_w_nvfp4_int8<QR>, dim3((nhalves + 256 * QR - 1) / (256 * QR)),
+                       dim3(256), 0, st, packed, sc16, scale2, q, s, nhalves);
     count_launch();
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// BF16 -> NVFP4 (gemm_fp4.rs, quantize_bf16_to_nvfp4).  One lane per 32
-// elements = two 16-element blocks: 64 bytes in, 16 packed bytes and two
-// E4M3 scales out.  sb = E4M3(fl(amax/fl(6*scale2))), d = fl(e4m3(sb)*scale2),
-// code = E2M1(fl(x/d)), or +0 everywhere when d == 0.
+// BF16 -> NVFP4 (gemm_fp4.rs, quantize_bf16_to_nvfp4).  A 16-element block
+// is held by two adjacent lanes, 8 elements (one 16-byte chunk) each, and
+// each lane writes its 8 codes as one dword.  sb = E4M3(fl(amax /
+// fl(6*scale2))), d = fl(e4m3(sb)*scale2), code = E2M1(fl(x/d)), or +0
+// everywhere when d == 0.  The block scales of four blocks (8 lanes) are
+// gathered into one dword store.
 // ---------------------------------------------------------------------------
+template <int QR>
 __global__ __launch_bounds__(256) void k_quantize_bf16_nvfp4(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ packed,
     uint8_t *__restrict__ sc16, float scale2, uint32_t nchunks)
 {
-    uint32_t c = blockIdx.x * 256u + threadIdx.x;
-    if (c >= nchunks)
-        return;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)c * 32);
-    u32x4 raw[4];
+    const uint32_t base = blockIdx.x * (256u * QR) + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    u32x4 raw[QR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        raw[i] = __builtin_nontemporal_load(src + i);
+    for (int u = 0; u < QR; ++u) {
+        const uint32_t c = base + 256u * u;
+        raw[u] = (u32x4){0, 0, 0, 0};
+        if (c < nchunks)
+            raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + (size_t)c * 8));
+    }
     const float six_s2 = 6.0f * scale2;
-    u32x4 out = {0, 0, 0, 0};
-    uint32_t scales = 0;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        float v[16];
+    for (int u = 0; u < QR; ++u) {
+        const uint32_t c = base + 256u * u;     // nchunks % 4 == 0: a block's lanes agree
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t wd = raw[2 * blk + i / 4][i % 4];
-            v[2 * i] = bf16_lo(wd);
-            v[2 * i + 1] = bf16_hi(wd);
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_lo(raw[u][i]);
+            v[2 * i + 1] = bf16_hi(raw[u][i]);
         }
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 8; ++i)
             amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-        uint32_t sb = enc_e4m3(div_rn(amax, six_s2));
-        float d = dec_e4m3(sb) * scale2;
-        scales |= sb << (8 * blk);
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+        const uint32_t sb = enc_e4m3(div_rn(amax, six_s2));
+        const float d = dec_e4m3(sb) * scale2;
+        uint32_t codes = 0;
         if (d != 0.0f) {
             ScaleDiv dv(d);
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
+            for (int i = 0; i < 8; ++i)
                 v[i] = dv(v[i]);
-            out[2 * blk] = cvt_e2m1x8(&v[0]);
-            out[2 * blk + 1] = cvt_e2m1x8(&v[8]);
+            codes = cvt_e2m1x8(v);
+        }
+        // scales of the blocks of lanes 8g .. 8g+7 (every other lane) -> lane 8g
+        const uint32_t w4 = sb | (__shfl_down(sb, 2, WAVE) << 8) |
+                            (__shfl_down(sb, 4, WAVE) << 16) | (__shfl_down(sb, 6, WAVE) << 24);
+        if (c < nchunks) {
+            *reinterpret_cast<uint32_t *>(packed + (size_t)c * 4) = codes;
+            if ((lane & 7) == 0) {
+                // c % 8 == 0, so block c/2 starts a 4-byte-aligned word
+                if (c + 8 <= nchunks)
+                    *reinterpret_cast<uint32_t *>(sc16 + (c >> 1)) = w4;
+                else
+                    *reinterpret_cast<uint16_t *>(sc16 + (c >> 1)) = (uint16_t)w4;  // 2 blocks left
+            }
         }
     }
-    *reinterpret_cast<u32x4 *>(packed + (size_t)c * 16) = out;
-    *reinterpret_cast<uint16_t *>(sc16 + (size_t)c * 2) = (uint16_t)scales;
 }
 
 hipError_t launch_quantize_bf16_nvfp4(const uint16_t *x, uint8_t *packed,
                                       uint8_t *sc16, float scale2, uint32_t rows,
                                       uint32_t k, hipStream_t st)
 {
-    uint32_t nchunks = (uint32_t)((uint64_t)rows * k / 32);
-    hipLaunchKernelGGL(k_quantize_bf16_nvfp4, dim3((nchunks + 255) / 256),
+    uint32_t nchunks = (uint32_t)((uint64_t)rows * k / 8);
+    constexpr int QR = 2;
+    hipLaunchKernelGGL(k_quantize_bf16_nvfp4<QR>, dim3((nchunks + 256 * QR - 1) / (256 * QR)),
                        dim3(256), 0, st, x, packed, sc16, scale2, nchunks);
     count_launch();
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Per-row kernels: one 256-thread workgroup per row.
+// Per-row kernels: one 256-thread workgroup per row (the block-scaled FP8
+// requant below also has a one-wave-per-row form).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float block_max_256(float v, float *red)
 {
@@ -426,20 +471,87 @@ __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_long(
         s[row] = sc;
 }
 
+// Rows of up to 64*CPL chunks: one wave per row (four rows per workgroup),
+// CPL 16-code chunks per lane in registers, the row absmax by wave shuffles
+// alone (no LDS, no barrier), every load / store instruction one contiguous
+// kilobyte (lane l takes chunks l, l + 64, ...), and the BF16 intermediate
+// kept packed (two values per register).
+template <int CPL>
+__global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_wave(
+    const uint8_t *__restrict__ w, const float *__restrict__ grid,
+    uint8_t *__restrict__ q, float *__restrict__ s, uint32_t n, uint32_t k)
+{
+    const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= n)
+        return;                          // the whole wave
+    const uint8_t *wr = w + (size_t)row * k;
+    const float *gr = grid + (size_t)(row / 128) * (k / 128);
+    const uint32_t nch = k / 16;
+    u32x4 raw[CPL];
+    float bs[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = lane + 64u * j;
+        raw[j] = (u32x4){0, 0, 0, 0};
+        bs[j] = 0.0f;
+        if (c < nch) {
+            raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr + (size_t)c * 16));
+            bs[j] = gr[(c * 16) / 128];
+        }
+    }
+    uint32_t yb[CPL][8];                 // BF16 pairs of the intermediate
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        float y[16];
+        blockfp8_to_bf16_vals(raw[j], bs[j], y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            yb[j][i] = (__float_as_uint(y[2 * i]) >> 16) | (__float_as_uint(y[2 * i + 1]) & 0xFFFF0000u);
+            amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(y[2 * i]),
+                                                         __builtin_fabsf(y[2 * i + 1])));
+        }
+    }
+    amax = wave_max(amax);
+    const float sc = div_rn(amax, 448.0f);
+    const ScaleDiv dv(sc);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = lane + 64u * j;
+        if (c < nch) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[2 * i] = bf16_lo(yb[j][i]);
+                v[2 * i + 1] = bf16_hi(yb[j][i]);
+            }
+            const u32x2 lo = enc8_e4m3(&v[0], dv, sc == 0.0f), hi = enc8_e4m3(&v[8], dv, sc == 0.0f);
+            *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+    }
+    if (lane == 0)
+        s[row] = sc;
+}
+
 hipError_t launch_requant_blockfp8_rowwise(const uint8_t *w, const float *grid,
                                            uint8_t *q, float *s, uint32_t n,
                                            uint32_t k, hipStream_t st)
 {
-    uint32_t nch = k / 16;
-    dim3 g(n), b(256);
-    if (nch <= 256)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise<1>, g, b, 0, st, w, grid, q, s, k);
-    else if (nch <= 512)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise<2>, g, b, 0, st, w, grid, q, s, k);
+    const uint32_t nch = k / 16;
+    const dim3 gw((n + 3) / 4), b(256);
+    if (nch <= 64 * 2)
+        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<2>, gw, b, 0, st, w, grid, q, s, n, k);
+    else if (nch <= 64 * 4)
+        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<4>, gw, b, 0, st, w, grid, q, s, n, k);
+    else if (nch <= 64 * 6)
+        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<6>, gw, b, 0, st, w, grid, q, s, n, k);
+    else if (nch <= 64 * 8)
+        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<8>, gw, b, 0, st, w, grid, q, s, n, k);
     else if (nch <= 1024)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise<4>, g, b, 0, st, w, grid, q, s, k);
+        hipLaunchKernelGGL(k_requant_blockfp8_rowwise<4>, dim3(n), b, 0, st, w, grid, q, s, k);
     else
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_long, g, b, 0, st, w, grid, q, s, k);
+        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_long, dim3(n), b, 0, st, w, grid, q, s, k);
     count_launch();
     return hipGetLastError();
 }
