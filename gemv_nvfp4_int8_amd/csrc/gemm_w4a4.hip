@@ -173,15 +173,229 @@ __global__ __launch_bounds__(256) void k_w4a4_gemm(
         }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile variant for K % 256 == 0, M >= 256, N >= 160: 256 x 160
+// workgroup tiles (M = 4096, N = 5120 makes 512 tiles, two rounds on 256
+// CUs), each wave a 128 x 80 block of 8 x 5 v_mfma_f32_16x16x32_f16 tiles,
+// so every converted fragment feeds 5 or 8 MFMAs.
+//
+// K advances in stages of 256 elements.  A stage buffer holds the packed
+// A panel (256 rows x 128 bytes), the packed W panel (160 rows), and the
+// 16 scale bytes of every row of both (W scale rows padded to 256 so each
+// wave issues the same loads); two buffers, filled by 16-byte LDS-DMA loads
+// a whole stage (~5000 MFMA cycles) ahead.  Packed rows are stored with the
+// 16-byte chunks XOR-swizzled by (row / 2) % 8, so 16 consecutive rows
+// reading one logical chunk hit distinct banks.
+//
+// K order: both operands must pair the same k, so any permutation shared by
+// A and W is allowed.  Lane group g (lane / 16) reads the 16 bytes (32
+// elements) at byte 64t + 16g of the stage row for four consecutive MFMA
+// K steps 4t + v (t = 0, 1; v = 0 .. 3) and feeds bytes 4v .. 4v+3 to step
+// 4t + v; those 8 elements lie in 16-element block 8t + 2g + v/2.
+//
+// The MFMAs compute C^T tiles (W fragment first): lane l holds row l % 16 of
+// its C tile and four consecutive columns 4*(l/16) .. +3, written as one
+// 8-byte store.  The last tile row / column is shifted back to end at M / N
+// (every loaded row exists) and stores only what the previous tile did not.
+// ---------------------------------------------------------------------------
+constexpr int WB_TM = 256, WB_TN = 160;
+constexpr int WB_KE = 256;                    // K elements per stage
+constexpr int WB_KB = WB_KE / 2;              // packed bytes per row per stage
+constexpr int WB_NS = WB_KE / 16;             // scale bytes per row per stage
+constexpr int WB_PA = 0;                      // byte offsets in a stage buffer
+constexpr int WB_PW = WB_PA + WB_TM * WB_KB;  // 32 KB
+constexpr int WB_SA = WB_PW + WB_TN * WB_KB;  // + 20 KB
+constexpr int WB_SW = WB_SA + WB_TM * WB_NS;  // + 4 KB
+constexpr int WB_BUF = WB_SW + 256 * WB_NS;   // + 4 KB = 60 KB
+
+__global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
+    const uint8_t *__restrict__ Ap, const uint8_t *__restrict__ Asc,
+    const uint8_t *__restrict__ Wp, const uint8_t *__restrict__ Wsc,
+    uint16_t *__restrict__ out, float s2, uint32_t M, uint32_t N, uint32_t K,
+    uint32_t mtiles, uint32_t ntiles)
+{
+    // Two stage buffers as separate LDS variables (distinct alias scopes:
+    // reading one need not wait for the DMA into the other).
+    __shared__ __attribute__((aligned(1024))) uint8_t B0[WB_BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t B1[WB_BUF];
+
+    uint32_t tm, tn;
+    tile_coords(mtiles, ntiles, tm, tn);
+    const uint32_t m0 = tm * WB_TM, n0 = tn * WB_TN;
+    const uint32_t m0e = min(m0, M - WB_TM), n0e = min(n0, N - WB_TN);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const uint32_t ldp = K / 2, lds_ = K / 16;         // packed / scale row strides
+    const uint32_t nst = K / WB_KE;
+
+    // ---- DMA addressing (instruction j of a wave fills one kilobyte:
+    // 8 packed rows x 128 bytes, lane -> row lane/8, physical chunk lane%8
+    // holding logical chunk (lane%8) ^ swz(row), swz(row) = ((kb & 1) << 2)
+    // | (lane >> 4) for kilobyte kb).
+    uint32_t dvo[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        dvo[e] = (uint32_t)(lane >> 3) * ldp + 16u * ((lane & 7) ^ ((e << 2) | (lane >> 4)));
+    const uint8_t *const a_rows = Ap + (size_t)(m0e + 64 * wave) * ldp;   // kb = 8w + j
+    const uint8_t *const w_rows = Wp + (size_t)(n0e + 8 * wave) * ldp;    // kb = w + 4j
+    const uint8_t *const as_row = Asc + (size_t)(m0e + 64 * wave + lane) * lds_;
+    const uint32_t wsr = n0e + 64 * wave + lane;
+    const uint8_t *const ws_row = Wsc + (size_t)(wsr < N ? wsr : N - 1) * lds_;
+    // Stage st into buffer B; stages past the end reload the last one (in
+    // bounds, never read) so every stage issues the same 15 loads per wave.
+    auto dma = [&](uint32_t st, uint8_t *B) {
+        const uint32_t s = st < nst ? st : nst - 1;
+        const uint8_t *pa = a_rows + s * WB_KB;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds(pa + (size_t)(8 * j) * ldp + dvo[j & 1],
+                                             (lds_void *)(B + WB_PA + 1024 * (8 * wave + j)), 16, 0, 0);
+        const uint8_t *pw = w_rows + s * WB_KB;
+#pragma unroll
+        for (int j = 0; j < 5; ++j)
+            __builtin_amdgcn_global_load_lds(pw + (size_t)(32 * j) * ldp + dvo[wave & 1],
+                                             (lds_void *)(B + WB_PW + 1024 * (wave + 4 * j)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(as_row + s * WB_NS, (lds_void *)(B + WB_SA + 1024 * wave), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ws_row + s * WB_NS, (lds_void *)(B + WB_SW + 1024 * wave), 16, 0, 0);
+    };
+
+    // ---- fragment reads: row 16*t + (lane % 16) of the wave's half, logical
+    // chunk 4*tt + g (tt = 0, 1), physical chunk ^ (((lane % 16) >> 1) & 7)
+    const int g = lane >> 4, r16 = lane & 15;
+    uint32_t lrow[2], lsc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        lrow[tt] = r16 * WB_KB + 16 * ((4 * tt + g) ^ ((r16 >> 1) & 7));
+        lsc[tt] = r16 * WB_NS + 8 * tt + 2 * g;         // the two block scales of the lane's 32
+    }
+    uint32_t lo[4];
+    auto launder = [&]() {
+        lo[0] = lrow[0];
+        lo[1] = lrow[1];
+        lo[2] = lsc[0];
+        lo[3] = lsc[1];
+        asm volatile("" : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]));
+    };
+
+    f32x4 acc[8][5];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 5; ++j)
+            acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // packed 16-byte reads and 2-byte scale pairs of one half-stage (tt)
+    struct Half {
+        u32x4 a[8], w[5];
+        uint32_t sa[8], sw[5];
+    };
+    auto read_half = [&](Half &h, const uint8_t *B, int tt) {
+        const uint8_t *pa = B + WB_PA + wm * 128 * WB_KB + lo[tt];
+        const uint8_t *pw = B + WB_PW + wn * 80 * WB_KB + lo[tt];
+        const uint8_t *qa = B + WB_SA + wm * 128 * WB_NS + lo[2 + tt];
+        const uint8_t *qw = B + WB_SW + wn * 80 * WB_NS + lo[2 + tt];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            h.a[t] = *reinterpret_cast<const u32x4 *>(pa + 16 * WB_KB * t);
+            h.sa[t] = *reinterpret_cast<const uint16_t *>(qa + 16 * WB_NS * t);
+        }
+#pragma unroll
+        for (int t = 0; t < 5; ++t) {
+            h.w[t] = *reinterpret_cast<const u32x4 *>(pw + 16 * WB_KB * t);
+            h.sw[t] = *reinterpret_cast<const uint16_t *>(qw + 16 * WB_NS * t);
+        }
+    };
+    // the 40 MFMAs of K step v of a half-stage
+    auto kstep = [&](const Half &h, int v) {
+        f16x8 fa[8], fw[5];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            fa[t] = fp4x8_scaled(h.a[t][v], e4m3_to_f16x2((h.sa[t] >> (8 * (v >> 1))) & 0xFFu));
+#pragma unroll
+        for (int t = 0; t < 5; ++t)
+            fw[t] = fp4x8_scaled(h.w[t][v], e4m3_to_f16x2((h.sw[t] >> (8 * (v >> 1))) & 0xFFu));
+#pragma unroll
+        for (int ti = 0; ti < 8; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 5; ++tj)
+                acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw[tj], fa[ti], acc[ti][tj], 0, 0, 0);
+    };
+    auto sync_all = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Stage st from buffer cur while stage st+1 is DMA'd into nxt (free: the
+    // barrier ending the previous stage came after every read of it).
+    auto stage = [&](uint32_t st, const uint8_t *cur, uint8_t *nxt) {
+        dma(st + 1, nxt);
+        launder();
+        Half h;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            read_half(h, cur, tt);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                kstep(h, v);
+        }
+        sync_all();
+    };
+
+    dma(0, B0);
+    sync_all();
+    uint32_t st = 0;
+    for (; st + 2 <= nst; st += 2) {
+        stage(st, B0, B1);
+        stage(st + 1, B1, B0);
+    }
+    if (st < nst)
+        stage(st, B0, B1);
+
+    // Epilogue: C[i][j] = bf16(s2 * acc); lane row i = ib + 16*ti, columns
+    // j = jb + 16*tj + c (c = 0..3).
+    const uint32_t ib = m0e + wm * 128 + r16;
+    const uint32_t jb = n0e + wn * 80 + 4 * g;
+    const bool fast = m0e == m0 && n0e == n0 && N % 4 == 0 &&
+                      reinterpret_cast<uintptr_t>(out) % 8 == 0;
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti) {
+        const uint32_t gi = ib + 16 * ti;
+#pragma unroll
+        for (int tj = 0; tj < 5; ++tj) {
+            const f32x4 c = acc[ti][tj];
+            const uint32_t gj = jb + 16 * tj;
+            if (fast) {
+                u32x2 pk;
+                pk[0] = pk_bf16(c[0] * s2, c[1] * s2);
+                pk[1] = pk_bf16(c[2] * s2, c[3] * s2);
+                *reinterpret_cast<u32x2 *>(out + (size_t)gi * N + gj) = pk;
+            } else if (gi >= m0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (gj + r >= n0)
+                        out[(size_t)gi * N + gj + r] = (uint16_t)f32_to_bf16(c[r] * s2);
+            }
+        }
+    }
+}
+
 hipError_t launch_w4a4_gemm(const uint8_t *ap, const uint8_t *asc,
                             const uint8_t *wp, const uint8_t *wsc, uint16_t *out,
                             float sa2, float sw2, uint32_t m, uint32_t n,
                             uint32_t k, hipStream_t st)
 {
-    uint32_t mt = (m + W4_BM - 1) / W4_BM, nt = (n + W4_BN - 1) / W4_BN;
     float s2 = sa2 * sw2;
-    hipLaunchKernelGGL(k_w4a4_gemm, dim3(mt * nt), dim3(256), 0, st,
-                       ap, asc, wp, wsc, out, s2, m, n, k, mt, nt);
+    if (k % WB_KE == 0 && m >= (uint32_t)WB_TM && n >= (uint32_t)WB_TN) {
+        uint32_t mt = (m + WB_TM - 1) / WB_TM, nt = (n + WB_TN - 1) / WB_TN;
+        hipLaunchKernelGGL(k_w4a4_gemm_big, dim3(mt * nt), dim3(256), 0, st,
+                           ap, asc, wp, wsc, out, s2, m, n, k, mt, nt);
+    } else {
+        uint32_t mt = (m + W4_BM - 1) / W4_BM, nt = (n + W4_BN - 1) / W4_BN;
+        hipLaunchKernelGGL(k_w4a4_gemm, dim3(mt * nt), dim3(256), 0, st,
+                           ap, asc, wp, wsc, out, s2, m, n, k, mt, nt);
+    }
     count_launch();
     return hipGetLastError();
 }

@@ -160,7 +160,12 @@ def test_int8_gemm_blockscaled_ragged(m, n, k):
     assert_gemm_close(host(out), oracle.int8_gemm_blockscaled(oa, ow, oas, ows), f"int8 {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(64, 96, 256), (33, 70, 160), (200, 300, 1024), (5, 130, 4096)])
+# Shapes cover both kernels: the 128 x 128 one and the 256 x 160 one (M >= 256,
+# N >= 160, K % 256 == 0) with one tile (256, 160), shifted last tiles
+# (300 x 330, 520 x 500), one stage, an even and an odd stage count, and
+# N % 4 != 0 (element-wise epilogue).
+@pytest.mark.parametrize("m,n,k", [(64, 96, 256), (33, 70, 160), (200, 300, 1024), (5, 130, 4096),
+                                   (256, 160, 256), (300, 330, 512), (520, 500, 1280), (257, 162, 768)])
 def test_w4a4_gemm_matches_oracle(m, n, k):
     a = _bf16_rows((m, k), 51 + m)
     w = _bf16_rows((n, k), 52 + n, std=0.02)
@@ -173,9 +178,9 @@ def test_w4a4_gemm_matches_oracle(m, n, k):
     assert_gemm_close(host(out), oracle.w4a4_gemm(ap, asc, wp, wsc, 1.0, sw2), f"w4a4 {m}x{n}x{k}")
 
 
-def test_w4a4_every_scale_code_and_nibble():
-    # All 16 E2M1 codes against all finite E4M3 scale codes.
-    m, n, k = 32, 128, 256
+@pytest.mark.parametrize("m,n,k", [(32, 128, 256), (256, 160, 512)])
+def test_w4a4_every_scale_code_and_nibble(m, n, k):
+    # All 16 E2M1 codes against all finite E4M3 scale codes, on both kernels.
     g = torch.Generator().manual_seed(3)
     ap = torch.randint(0, 256, (m, k // 2), generator=g, dtype=torch.int32).to(torch.uint8)
     wp = torch.randint(0, 256, (n, k // 2), generator=g, dtype=torch.int32).to(torch.uint8)
