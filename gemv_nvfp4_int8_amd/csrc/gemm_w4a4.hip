@@ -208,12 +208,20 @@ constexpr int WB_SA = WB_PW + WB_TN * WB_KB;  // + 20 KB
 constexpr int WB_SW = WB_SA + WB_TM * WB_NS;  // + 4 KB
 constexpr int WB_BUF = WB_SW + 256 * WB_NS;   // + 4 KB = 60 KB
 
-__global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
+// WM waves along M (2 or 4) times 2 along N: a wave owns RW = 256 / WM rows
+// (NA = RW / 16 MFMA tiles) by 80 columns (5 tiles).  WM = 4 runs two waves
+// per SIMD (512 threads, at most 256 registers each).
+template <int WM>
+__global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     const uint8_t *__restrict__ Ap, const uint8_t *__restrict__ Asc,
     const uint8_t *__restrict__ Wp, const uint8_t *__restrict__ Wsc,
     uint16_t *__restrict__ out, float s2, uint32_t M, uint32_t N, uint32_t K,
     uint32_t mtiles, uint32_t ntiles)
 {
+    constexpr int NW = 2 * WM;            // waves
+    constexpr int RW = WB_TM / WM;        // rows per wave
+    constexpr int NA = RW / 16;           // A tiles per wave
+    constexpr int APW = 32 / NW;          // A packed kilobytes per wave
     // Two stage buffers as separate LDS variables (distinct alias scopes:
     // reading one need not wait for the DMA into the other).
     __shared__ __attribute__((aligned(1024))) uint8_t B0[WB_BUF];
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
     const uint32_t m0e = min(m0, M - WB_TM), n0e = min(n0, N - WB_TN);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
     const uint32_t ldp = K / 2, lds_ = K / 16;         // packed / scale row strides
     const uint32_t nst = K / WB_KE;
 
@@ -237,27 +245,35 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
 #pragma unroll
     for (int e = 0; e < 2; ++e)
         dvo[e] = (uint32_t)(lane >> 3) * ldp + 16u * ((lane & 7) ^ ((e << 2) | (lane >> 4)));
-    const uint8_t *const a_rows = Ap + (size_t)(m0e + 64 * wave) * ldp;   // kb = 8w + j
-    const uint8_t *const w_rows = Wp + (size_t)(n0e + 8 * wave) * ldp;    // kb = w + 4j
-    const uint8_t *const as_row = Asc + (size_t)(m0e + 64 * wave + lane) * lds_;
-    const uint32_t wsr = n0e + 64 * wave + lane;
+    // A kilobytes kb = APW*w + j; W kilobytes kb = w + NW*j (kb < 20; the
+    // parity of kb, which picks the swizzle, is then that of j, resp. w);
+    // the 4 A-scale and 4 W-scale kilobytes (64 rows each) go to waves
+    // i and i + 4 (NW = 8) or both to wave i (NW = 4).
+    const uint8_t *const a_rows = Ap + (size_t)(m0e + 8 * APW * wave) * ldp;
+    const uint8_t *const w_rows = Wp + (size_t)(n0e + 8 * wave) * ldp;
+    const int sq = wave & 3;
+    const uint8_t *const as_row = Asc + (size_t)(m0e + 64 * sq + lane) * lds_;
+    const uint32_t wsr = n0e + 64 * sq + lane;
     const uint8_t *const ws_row = Wsc + (size_t)(wsr < N ? wsr : N - 1) * lds_;
-    // Stage st into buffer B; stages past the end reload the last one (in
-    // bounds, never read) so every stage issues the same 15 loads per wave.
+    // Stage st into buffer B (stages past the end reload the last one: in
+    // bounds, never read).
     auto dma = [&](uint32_t st, uint8_t *B) {
         const uint32_t s = st < nst ? st : nst - 1;
         const uint8_t *pa = a_rows + s * WB_KB;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < APW; ++j)
             __builtin_amdgcn_global_load_lds(pa + (size_t)(8 * j) * ldp + dvo[j & 1],
-                                             (lds_void *)(B + WB_PA + 1024 * (8 * wave + j)), 16, 0, 0);
+                                             (lds_void *)(B + WB_PA + 1024 * (APW * wave + j)), 16, 0, 0);
         const uint8_t *pw = w_rows + s * WB_KB;
 #pragma unroll
-        for (int j = 0; j < 5; ++j)
-            __builtin_amdgcn_global_load_lds(pw + (size_t)(32 * j) * ldp + dvo[wave & 1],
-                                             (lds_void *)(B + WB_PW + 1024 * (wave + 4 * j)), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(as_row + s * WB_NS, (lds_void *)(B + WB_SA + 1024 * wave), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ws_row + s * WB_NS, (lds_void *)(B + WB_SW + 1024 * wave), 16, 0, 0);
+        for (int j = 0; j < (20 + NW - 1) / NW; ++j)
+            if (wave + NW * j < 20)
+                __builtin_amdgcn_global_load_lds(pw + (size_t)(8 * NW * j) * ldp + dvo[wave & 1],
+                                                 (lds_void *)(B + WB_PW + 1024 * (wave + NW * j)), 16, 0, 0);
+        if (NW == 4 || wave < 4)
+            __builtin_amdgcn_global_load_lds(as_row + s * WB_NS, (lds_void *)(B + WB_SA + 1024 * sq), 16, 0, 0);
+        if (NW == 4 || wave >= 4)
+            __builtin_amdgcn_global_load_lds(ws_row + s * WB_NS, (lds_void *)(B + WB_SW + 1024 * sq), 16, 0, 0);
     };
 
     // ---- fragment reads: row 16*t + (lane % 16) of the wave's half, logical
@@ -278,25 +294,25 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
         asm volatile("" : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]));
     };
 
-    f32x4 acc[8][5];
+    f32x4 acc[NA][5];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int j = 0; j < 5; ++j)
             acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // packed 16-byte reads and 2-byte scale pairs of one half-stage (tt)
     struct Half {
-        u32x4 a[8], w[5];
-        uint32_t sa[8], sw[5];
+        u32x4 a[NA], w[5];
+        uint32_t sa[NA], sw[5];
     };
     auto read_half = [&](Half &h, const uint8_t *B, int tt) {
-        const uint8_t *pa = B + WB_PA + wm * 128 * WB_KB + lo[tt];
+        const uint8_t *pa = B + WB_PA + wm * RW * WB_KB + lo[tt];
         const uint8_t *pw = B + WB_PW + wn * 80 * WB_KB + lo[tt];
-        const uint8_t *qa = B + WB_SA + wm * 128 * WB_NS + lo[2 + tt];
+        const uint8_t *qa = B + WB_SA + wm * RW * WB_NS + lo[2 + tt];
         const uint8_t *qw = B + WB_SW + wn * 80 * WB_NS + lo[2 + tt];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < NA; ++t) {
             h.a[t] = *reinterpret_cast<const u32x4 *>(pa + 16 * WB_KB * t);
             h.sa[t] = *reinterpret_cast<const uint16_t *>(qa + 16 * WB_NS * t);
         }
@@ -306,17 +322,22 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
             h.sw[t] = *reinterpret_cast<const uint16_t *>(qw + 16 * WB_NS * t);
         }
     };
-    // the 40 MFMAs of K step v of a half-stage
-    auto kstep = [&](const Half &h, int v) {
-        f16x8 fa[8], fw[5];
+    // the 40 MFMAs of K step v of a half-stage; sc* hold the FP16 values of a
+    // fragment's two block scales (the packed FP8 converter, exact for E4M3)
+    auto kstep = [&](const Half &h, const f16x2 *sca, const f16x2 *scw, int v) {
+        f16x8 fa[NA], fw[5];
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-            fa[t] = fp4x8_scaled(h.a[t][v], e4m3_to_f16x2((h.sa[t] >> (8 * (v >> 1))) & 0xFFu));
+        for (int t = 0; t < NA; ++t) {
+            const _Float16 sb = sca[t][v >> 1];
+            fa[t] = fp4x8_scaled(h.a[t][v], (f16x2){sb, sb});
+        }
 #pragma unroll
-        for (int t = 0; t < 5; ++t)
-            fw[t] = fp4x8_scaled(h.w[t][v], e4m3_to_f16x2((h.sw[t] >> (8 * (v >> 1))) & 0xFFu));
+        for (int t = 0; t < 5; ++t) {
+            const _Float16 sb = scw[t][v >> 1];
+            fw[t] = fp4x8_scaled(h.w[t][v], (f16x2){sb, sb});
+        }
 #pragma unroll
-        for (int ti = 0; ti < 8; ++ti)
+        for (int ti = 0; ti < NA; ++ti)
 #pragma unroll
             for (int tj = 0; tj < 5; ++tj)
                 acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw[tj], fa[ti], acc[ti][tj], 0, 0, 0);
@@ -336,9 +357,16 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             read_half(h, cur, tt);
+            f16x2 sca[NA], scw[5];
+#pragma unroll
+            for (int t = 0; t < NA; ++t)
+                sca[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h.sa[t], 1.0f, false);
+#pragma unroll
+            for (int t = 0; t < 5; ++t)
+                scw[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h.sw[t], 1.0f, false);
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                kstep(h, v);
+                kstep(h, sca, scw, v);
         }
         sync_all();
     };
@@ -355,12 +383,12 @@ __global__ __launch_bounds__(256, 1) void k_w4a4_gemm_big(
 
     // Epilogue: C[i][j] = bf16(s2 * acc); lane row i = ib + 16*ti, columns
     // j = jb + 16*tj + c (c = 0..3).
-    const uint32_t ib = m0e + wm * 128 + r16;
+    const uint32_t ib = m0e + wm * RW + r16;
     const uint32_t jb = n0e + wn * 80 + 4 * g;
     const bool fast = m0e == m0 && n0e == n0 && N % 4 == 0 &&
                       reinterpret_cast<uintptr_t>(out) % 8 == 0;
 #pragma unroll
-    for (int ti = 0; ti < 8; ++ti) {
+    for (int ti = 0; ti < NA; ++ti) {
         const uint32_t gi = ib + 16 * ti;
 #pragma unroll
         for (int tj = 0; tj < 5; ++tj) {
@@ -389,7 +417,9 @@ hipError_t launch_w4a4_gemm(const uint8_t *ap, const uint8_t *asc,
     float s2 = sa2 * sw2;
     if (k % WB_KE == 0 && m >= (uint32_t)WB_TM && n >= (uint32_t)WB_TN) {
         uint32_t mt = (m + WB_TM - 1) / WB_TM, nt = (n + WB_TN - 1) / WB_TN;
-        hipLaunchKernelGGL(k_w4a4_gemm_big, dim3(mt * nt), dim3(256), 0, st,
+        // WM = 2 (four waves, 128 x 80 each): two waves per SIMD (WM = 4)
+        // measured slower at 4096 x 5120 x 17408 (778 vs 736 us)
+        hipLaunchKernelGGL(k_w4a4_gemm_big<2>, dim3(mt * nt), dim3(256), 0, st,
                            ap, asc, wp, wsc, out, s2, m, n, k, mt, nt);
     } else {
         uint32_t mt = (m + W4_BM - 1) / W4_BM, nt = (n + W4_BN - 1) / W4_BN;
