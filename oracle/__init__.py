@@ -75,6 +75,7 @@ def lib():
         L.oracle_int8_gemm_blockscaled.argtypes = [P, P, P, P, P, I, I, I]
         L.oracle_w4a4_gemm.argtypes = [P, P, P, P, P, F, F, I, I, I]
         L.oracle_fp8_gemv_rowscale.argtypes = [P, P, P, P, I, I, I]
+        L.oracle_fp8_gemv_blockscale.argtypes = [P, P, P, P, I, I, I]
         L.oracle_fp8_gemm_rowscale.argtypes = [P, P, P, P, P, I, I, I]
         L.oracle_num_threads.restype = ctypes.c_int
         for fn in ("oracle_requant_a_bf16_int8", "oracle_requant_w_nvfp4_int8",
@@ -82,7 +83,7 @@ def lib():
                    "oracle_requant_w_blockfp8_rowwise",
                    "oracle_int8_block_partials", "oracle_int8_gemm_blockscaled",
                    "oracle_w4a4_gemm", "oracle_fp8_gemv_rowscale",
-                   "oracle_fp8_gemm_rowscale"):
+                   "oracle_fp8_gemv_blockscale", "oracle_fp8_gemm_rowscale"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -248,6 +249,20 @@ def fp8_gemv_rowscale(x_bf16, w, row_scale) -> np.ndarray:
     assert w.shape[1] == k and row_scale.shape == (n,)
     out = np.empty((m, n), np.uint16)
     lib().oracle_fp8_gemv_rowscale(_p(x), _p(w), _p(row_scale), _p(out), m, n, k)
+    return out
+
+
+def fp8_gemv_blockscale(x_bf16, w, block_scale) -> np.ndarray:
+    """BF16 [m,k] x E4M3 [n,k] with F32 block scales [n/128, k/128] -> BF16 bits [m,n]."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w, np.uint8)
+    block_scale = _c(block_scale, np.float32)
+    m, k = x.shape
+    n = w.shape[0]
+    assert w.shape[1] == k and n % 128 == 0 and k % 128 == 0
+    assert block_scale.shape == (n // 128, k // 128)
+    out = np.empty((m, n), np.uint16)
+    lib().oracle_fp8_gemv_blockscale(_p(x), _p(w), _p(block_scale), _p(out), m, n, k)
     return out
 
 

@@ -404,6 +404,29 @@ void oracle_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
         }
 }
 
+/* fp8_gemv_batch.rs, w8a16_gemv / w8a16_gemv_batch2 / w8a16_gemv_batch4: BF16
+ * x [m,k] times a block-scaled E4M3 weight [n,k] whose F32 scale grid s
+ * [n/128, k/128] holds one scale per 128 x 128 block:
+ *   C[i,j] = bf16( sum_t x[i,t] * e4m3(w[j,t]) * s[j/128, t/128] ).
+ * Each product is exact in binary64 (8 + 4 + 24 significant bits), so only
+ * the sum and the final BF16 rounding round. */
+void oracle_fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
+                                const float *s, uint16_t *out,
+                                int64_t m, int64_t n, int64_t k)
+{
+    const int64_t kb = k / 128;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = 0; i < m; ++i) {
+            const float *srow = s + (j / 128) * kb;
+            double c = 0.0;
+            for (int64_t t = 0; t < k; ++t)
+                c += (double)oracle_bf16_to_float(x[i * k + t]) *
+                     oracle_e4m3_decode(w[j * k + t]) * (double)srow[t / 128];
+            out[i * n + j] = oracle_bf16_from_double(c);
+        }
+}
+
 /* dispatch_proj_rowwise.rs, cublas_fp8_rowwise_proj (the row-wise FP8 GEMM
  * it ends in): C = bf16(sa[m] * sw[n] * sum_k e4m3(a[m,k]) * e4m3(w[n,k])). */
 void oracle_fp8_gemm_rowscale(const uint8_t *a, const float *sa,

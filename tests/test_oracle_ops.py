@@ -359,3 +359,76 @@ def test_fp8_gemm_rowscale_rational_and_zero_rows():
             tot = sum(Fraction(oracle.e4m3_decode(a[i, t])) * Fraction(oracle.e4m3_decode(w[j, t]))
                       for t in range(k))
             assert c[i, j] == _bf16_exact(Fraction(float(sa[i])) * Fraction(float(sw[j])) * tot)
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled FP8 GEMV (fp8_gemv_batch.rs, w8a16_gemv / _batch2 / _batch4):
+# C[i,j] = bf16(sum_t x[i,t] * e4m3(w[j,t]) * s[j/128, t/128]).
+def _blockscale_case(seed, m, n, k):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.standard_normal(m * k)).reshape(m, k)
+    w = rng.integers(0, 0x7F, (n, k), dtype=np.uint8) | \
+        (rng.integers(0, 2, (n, k), dtype=np.uint8) << 7)
+    s = rng.uniform(1e-3, 1e-1, (n // 128, k // 128)).astype(np.float32)
+    return x, w, s
+
+
+def test_fp8_gemv_blockscale_rational():
+    # Exact rationals: every product carries the scale of its own 128 x 128
+    # block (two N blocks, two K blocks, all four scales distinct).
+    x, w, s = _blockscale_case(21, 2, 256, 256)
+    c = oracle.fp8_gemv_blockscale(x, w, s)
+    xf = oracle.bf16_bits_to_f32(x).astype(np.float64)
+    for i in range(2):
+        for j in (0, 1, 63, 127, 128, 200, 255):
+            tot = sum(Fraction(float(xf[i, t])) * Fraction(oracle.e4m3_decode(w[j, t])) *
+                      Fraction(float(s[j // 128, t // 128])) for t in range(256))
+            assert c[i, j] == _bf16_exact(tot)
+
+
+def test_fp8_gemv_blockscale_unit_grid_is_bf16_of_f64_matmul():
+    # With every block scale 1 the GEMV is a plain product: numpy's f64
+    # matmul of the decoded operands, rounded to BF16 (its summation order
+    # differs, so allow one BF16 ulp on the rare value next to a tie).
+    x, w, _ = _blockscale_case(22, 4, 128, 384)
+    s = np.ones((1, 3), np.float32)
+    c = oracle.fp8_gemv_blockscale(x, w, s).astype(np.int64)
+    wf = np.vectorize(oracle.e4m3_decode)(w).astype(np.float64)
+    ref = oracle.bf16_bits_to_f32(x).astype(np.float64) @ wf.T
+    ref_bits = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    ref_bits = ref_bits.astype(np.int64) & 0xFFFF
+    diff = np.abs(c - ref_bits)
+    assert diff.max() <= 1 and np.mean(diff == 0) > 0.99
+
+
+def test_fp8_gemv_blockscale_single_live_k_block_is_a_row_scaled_slice():
+    # A grid that is zero outside K block 1 computes that block's 128-column
+    # slice alone, with the block's scale acting as a row scale (the
+    # row-scaled GEMV, pinned separately above, on the slice).
+    x, w, s = _blockscale_case(23, 3, 256, 384)
+    s[:, 0] = 0.0
+    s[:, 2] = 0.0
+    c = oracle.fp8_gemv_blockscale(x, w, s)
+    rs = np.repeat(s[:, 1], 128).astype(np.float32)
+    ref = oracle.fp8_gemv_rowscale(np.ascontiguousarray(x[:, 128:256]),
+                                   np.ascontiguousarray(w[:, 128:256]), rs)
+    assert np.array_equal(c, ref)
+
+
+def test_fp8_gemv_blockscale_power_of_two_grid_scales_exactly():
+    # Doubling every block scale doubles every output exactly (no overflow
+    # at these magnitudes): BF16 exponent + 1, same mantissa.
+    x, w, s = _blockscale_case(24, 2, 128, 256)
+    c1 = oracle.fp8_gemv_blockscale(x, w, s).astype(np.int64)
+    c2 = oracle.fp8_gemv_blockscale(x, w, (s * 2).astype(np.float32)).astype(np.int64)
+    nz = (c1 & 0x7FFF) != 0
+    assert np.array_equal(c2[nz], c1[nz] + (1 << 7))
+
+
+def test_fp8_gemv_blockscale_batched_rows_equal_single_row_calls():
+    # The pages' invariant (w8a16_gemv_batch4 is bit-identical per row to
+    # w8a16_gemv).
+    x, w, s = _blockscale_case(25, 4, 128, 256)
+    full = oracle.fp8_gemv_blockscale(x, w, s)
+    for i in range(4):
+        assert np.array_equal(full[i:i + 1], oracle.fp8_gemv_blockscale(x[i:i + 1], w, s))
