@@ -16,8 +16,10 @@ The same line carries:
                 bytes per launch, and the fraction of the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same step;
   secondary     every other row of the hot path at its own workload size:
-                quantizers / requantizers in GB/s against HBM, and the three
-                GEMMs in TFLOP/s against the MFMA peak of their data type.
+                quantizers / requantizers in GB/s against HBM, the three
+                GEMMs in TFLOP/s against the MFMA peak of their data type,
+                and the block-scaled FP8 GEMV (128 x 128 F32 block scales)
+                at the decode shapes for M in {1, 2, 4}, in GB/s.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
 """
@@ -302,6 +304,34 @@ def run_secondary(qp, synth, dev, only):
             ent[f"frac_{d}"] = round(tf / PEAK_TFLOPS[d], 4)
         res[name] = ent
         log(f"  {name}: {ms*1e3:.1f} us  {tf:.1f} TFLOP/s ({tf / PEAK_TFLOPS[dtype_peak]:.1%} of {dtype_peak})")
+
+    # Block-scaled FP8 GEMV (128 x 128 F32 block scales) at the decode shapes,
+    # M in {1, 2, 4}; weights rotate over copies of >= 1 GiB per shape.
+    if want("fp8_gemv_blockscale"):
+        rows = []
+        for sid, (n, k) in enumerate(GEMV_SHAPES):
+            w, grid = synth.gemv_block_weight(n, k, dev, shape_id=sid)
+            copies = [(w, grid)] + [(w.clone(), grid.clone())
+                                    for _ in range(rot_count(n * k) - 1)]
+            x = synth.gemv_acts_bf16(4, k, dev, shape_id=sid)
+            for m in (1, 2, 4):
+                o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                xm = x[:m]
+                ms = time_launches(lambda i: qp.fp8_gemv_blockscale(
+                    xm, copies[i % len(copies)][0], copies[i % len(copies)][1], o),
+                    iters=max(20, 2 * len(copies)))
+                wbytes = n * k + (n // 128) * (k // 128) * 4
+                abytes = wbytes + 2 * m * k + 2 * m * n
+                gbs = abytes / (ms * 1e-3) / 1e9
+                rows.append({"n": n, "k": k, "m": m, "us": round(ms * 1e3, 2),
+                             "weight_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                             "algorithmic_GBs": round(gbs, 1),
+                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+                log(f"  fp8_gemv_blockscale N={n} M={m}: {ms*1e3:.2f} us  "
+                    f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
+            del w, grid, copies, x
+            torch.cuda.empty_cache()
+        res["fp8_gemv_blockscale"] = rows
 
     # W4A8 prefill: NVFP4 weight 17408x5120 -> int8; acts 2048x5120.
     if want("w4a8") or want("requant_a_bf16_int8") or want("requant_w_nvfp4_int8") \

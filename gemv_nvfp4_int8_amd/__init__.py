@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "fp8_gemm_rowscale": [P, P, P, P, P, U, U, U, P],
             "fp8_rowwise_proj": [I, P, P, P, P, P, P, P, P, U, U, U, P],
             "fp8_gemv_rowscale": [P, P, P, P, U, U, U, P],
+            "fp8_gemv_blockscale": [P, P, P, P, U, U, U, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -299,10 +300,22 @@ def fp8_gemv_rowscale(x, w, row_scale, out, stream=None):
         _ptr(x), _ptr(w), _ptr(row_scale), _ptr(out), m, n, k, _stream(stream)))
 
 
+def fp8_gemv_blockscale(x, w, block_scale, out, stream=None):
+    m, k = x.shape
+    n = w.shape[0]
+    _need(x, "x", BF16, (m, k))
+    _need(w, "w", U8, (n, k))
+    _need(block_scale, "block_scale", F32, (n // 128, k // 128))
+    _need(out, "out", BF16, (m, n))
+    _check("fp8_gemv_blockscale", lib().fp8_gemv_blockscale(
+        _ptr(x), _ptr(w), _ptr(block_scale), _ptr(out), m, n, k, _stream(stream)))
+
+
 __all__ = [
     "requant_w_nvfp4_int8", "requant_a_bf16_int8", "int8_gemm_blockscaled",
     "int8_w4a8_prefill", "int8_gemm_block_partials", "quantize_bf16_nvfp4",
     "w4a4_gemm", "requant_w_blockfp8_rowwise", "quant_rowwise_fp8",
     "fp8_gemm_rowscale", "fp8_rowwise_proj", "fp8_gemv_rowscale",
+    "fp8_gemv_blockscale",
     "launch_count", "status_string", "abi_version", "lib", "QProjError",
 ]

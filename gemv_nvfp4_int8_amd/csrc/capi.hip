@@ -253,4 +253,17 @@ int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
     return done(qp::launch_fp8_gemv_rowscale(x, w, row_scale, out, m, n, k, S(stream)));
 }
 
+int fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
+                        const float *block_scale, uint16_t *out, uint32_t m,
+                        uint32_t n, uint32_t k, void *stream)
+{
+    if (int e = check_ptrs({x, w, block_scale, out}))
+        return e;
+    if (m < 1 || m > 16)
+        return QP_ERR_RANGE;
+    if (n == 0 || k == 0 || n % 128 != 0 || k % 128 != 0 || !fits(n, k) || !fits(m, n))
+        return QP_ERR_SHAPE;
+    return done(qp::launch_fp8_gemv_blockscale(x, w, block_scale, out, m, n, k, S(stream)));
+}
+
 } // extern "C"

@@ -1,8 +1,17 @@
-// gemv_fp8.hip -- row-scaled FP8 GEMV for decode / verify batches (M <= 16)
-// on gfx950 (fp8_gemv_batch.rs: fp8_gemv_rowscale_batch8_rt2 /
-// _batch16_rt2 / dense_gemv_fp8w_batch2).
+// gemv_fp8.hip -- FP8-weight GEMVs for decode / verify batches (M <= 16) on
+// gfx950 (fp8_gemv_batch.rs).  Two scale layouts share the kernels:
 //
-//   C[i,j] = bf16( row_scale[j] * sum_t x[i,t] * e4m3(w[j,t]) )
+//   row-scaled    (fp8_gemv_rowscale_batch8_rt2 / _batch16_rt2,
+//                  dense_gemv_fp8w_batch2)
+//       C[i,j] = bf16( row_scale[j] * sum_t x[i,t] * e4m3(w[j,t]) )
+//   block-scaled  (w8a16_gemv / _batch2 / _batch4; one F32 scale per
+//                  128 x 128 weight block, grid S[N/128, K/128])
+//       C[i,j] = bf16( sum_t x[i,t] * e4m3(w[j,t]) * S[j/128, t/128] )
+//
+// The block-scaled form accumulates each 128-element K block of the
+// contraction in a fresh F32 partial and folds it into the running sum with
+// one FMA by that block's scale; a wave's rows always lie in one 128-row
+// block, so the scale is a wave-uniform scalar.
 //
 // Design (MI355X-first):
 //  * The contraction runs on MFMA, not on the vector ALU: at 8 TB/s an M=16
@@ -68,15 +77,28 @@ template <int T>
 struct GvSeg {
     u32x4 w[4 * T];     // 4T instructions of 4 rows x 256 B
     u32x4 x[2];         // 2 x 16 B of the workgroup's activation segment
+    float s[2];         // block scales of the segment's two K blocks (BS)
 };
 
-template <int T, int D>
+// Fold a 128-element block partial into the running sum: acc += s * p, one
+// rounding per element.
+__device__ __forceinline__ void fold_block(f32x4 &acc, float s, const f32x4 &p)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_fmaf(s, p[i], acc[i]);
+}
+
+// rs: the row scale [n] (BS = false) or the block scale grid [n/128, k/128]
+// (BS = true, n and k multiples of 128).
+template <int T, int D, bool BS>
 __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
     const float *__restrict__ rs, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k)
 {
     constexpr int ROWS = 16 * T;
+    static_assert(128 % ROWS == 0, "a wave's rows must share one 128-row scale block");
     __shared__ __attribute__((aligned(16))) uint8_t sw[4][ROWS * GV_WPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t sx[2][16 * GV_XPITCH];
 
@@ -85,6 +107,8 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
     const int col = lane & 15, grp = lane >> 4;
     const uint32_t row0 = blockIdx.x * (4 * ROWS) + wave * ROWS;
     const uint32_t nseg = (k + GV_SEG - 1) / GV_SEG;
+    const uint32_t kbl = k / 128;
+    const float *srow = rs + (size_t)((row0 < n ? row0 : n - 1) / 128) * kbl;
 
     // Weight loads: instruction j covers rows row0 + 4j .. + 3, lane -> row
     // 4j + grp, bytes 16*col of the segment.  Rows past n re-read row n-1.
@@ -108,6 +132,13 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
     auto load = [&](GvSeg<T> &g, uint32_t seg) {
         uint32_t kb = seg * GV_SEG;
         bool full = kb + GV_SEG <= k;
+        if constexpr (BS) {
+            // issued ahead of the weights, so the wait at the top of the
+            // segment that uses them covers them (the second index is
+            // clamped in bounds; a missing block is never folded)
+            g.s[0] = srow[2 * seg];
+            g.s[1] = srow[min(2 * seg + 1, kbl - 1)];
+        }
 #pragma unroll
         for (int j = 0; j < 4 * T; ++j) {
             uint32_t kk = kb + 16 * col;
@@ -139,6 +170,13 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 #pragma unroll
     for (int t = 0; t < T; ++t)
         acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // BS: the last block partial not yet folded, and its scale (a zero
+    // partial with scale 0 before the first segment)
+    f32x4 p_pend[T];
+    float s_pend = 0.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        p_pend[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     GvSeg<T> g[D];
 #pragma unroll
@@ -150,6 +188,10 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
         const int buf = seg & 1;
         GvSeg<T> &cur = g[0];
         stash(cur, buf);
+        // The second block of a segment may lie past K (K an odd number of
+        // 128-blocks); its partial is zero and it is folded with scale 0.
+        const float s_lo = cur.s[0];
+        const float s_hi = 2 * seg + 1 < kbl ? cur.s[1] : 0.f;
         // rotate the prefetch queue and refill its tail
 #pragma unroll
         for (int d = 0; d + 1 < D; ++d)
@@ -157,6 +199,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
         if (seg + D < nseg)
             load(g[D - 1], seg + D);
         __syncthreads();
+        f32x4 p[2][T];      // partials of the segment's two K blocks (BS)
 #pragma unroll
         for (int u = 0; u < GV_SEG / 64; ++u) {
             // lane (col, grp): activation row col, k = 64u + 16 grp .. +15
@@ -169,22 +212,56 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
                     &sw[wave][(16 * t + col) * GV_WPITCH + 64 * u + 16 * grp]);
                 bf16x8 blo, bhi;
                 fp8x16_to_bf16(wv, blo, bhi);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
+                if constexpr (BS) {
+                    f32x4 &pb = p[u / 2][t];
+                    if (u % 2 == 0)
+                        pb = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, pb, 0, 0, 0);
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, pb, 0, 0, 0);
+                } else {
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
+                }
+            }
+            if constexpr (BS) {
+                // Folds trail the MFMAs that produce them by one K step, so
+                // the MFMA results are not waited for: the previous
+                // segment's second block after this segment's first step,
+                // this segment's first block after its third step.  The
+                // order of the additions is still block by block along K.
+                if (u == 0)
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        fold_block(acc[t], s_pend, p_pend[t]);
+                if (u == 2)
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        fold_block(acc[t], s_lo, p[0][t]);
             }
         }
+        if constexpr (BS) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                p_pend[t] = p[1][t];
+            s_pend = s_hi;
+        }
     }
+    if constexpr (BS)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            fold_block(acc[t], s_pend, p_pend[t]);
 
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         uint32_t nn = row0 + 16u * t + col;
         if (nn < n) {
-            float sc = rs[nn];
+            float sc = BS ? 1.0f : rs[nn];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t mm = 4u * grp + i;
                 if (mm < m)
-                    out[(size_t)mm * n + nn] = (uint16_t)f32_to_bf16(acc[t][i] * sc);
+                    out[(size_t)mm * n + nn] =
+                        (uint16_t)f32_to_bf16(BS ? acc[t][i] : acc[t][i] * sc);
             }
         }
     }
@@ -202,15 +279,17 @@ template <int T>
 struct GvSegW {
     u32x4 w[4 * T];
     u32x4 x[8];          // 16 rows x 256 bf16 = 512 chunks of 16 B, 8 per lane
+    float s[2];          // block scales of the segment's two K blocks (BS)
 };
 
-template <int T, int D>
+template <int T, int D, bool BS>
 __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
     const float *__restrict__ rs, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k)
 {
     constexpr int ROWS = 16 * T;
+    static_assert(128 % ROWS == 0, "a workgroup's rows must share one 128-row scale block");
     __shared__ __attribute__((aligned(16))) uint8_t sw[4][ROWS * GV_WPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t sx[4][16 * GV_XPITCH];
     __shared__ f32x4 red[3][T][WAVE];
@@ -221,6 +300,8 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     const uint32_t nseg = (k + GV_SEG - 1) / GV_SEG;
     const uint32_t per = (nseg + 3) / 4;
     const uint32_t s_beg = min(nseg, per * wave), s_end = min(nseg, s_beg + per);
+    const uint32_t kbl = k / 128;
+    const float *srow = rs + (size_t)((row0 < n ? row0 : n - 1) / 128) * kbl;
 
     const uint8_t *wsrc[4 * T];
 #pragma unroll
@@ -239,6 +320,10 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     auto load = [&](GvSegW<T> &g, uint32_t seg) {
         uint32_t kb = seg * GV_SEG;
         bool full = kb + GV_SEG <= k;
+        if constexpr (BS) {
+            g.s[0] = srow[2 * seg];
+            g.s[1] = srow[min(2 * seg + 1, kbl - 1)];
+        }
 #pragma unroll
         for (int j = 0; j < 4 * T; ++j) {
             g.w[j] = (u32x4){0, 0, 0, 0};
@@ -268,6 +353,13 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 #pragma unroll
     for (int t = 0; t < T; ++t)
         acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // BS: the last block partial not yet folded, and its scale (a zero
+    // partial with scale 0 before the first segment)
+    f32x4 p_pend[T];
+    float s_pend = 0.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        p_pend[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     GvSegW<T> g[D];
 #pragma unroll
@@ -277,11 +369,16 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 
     for (uint32_t seg = s_beg; seg < s_end; ++seg) {
         stash(g[0]);
+        // The second block of a segment may lie past K (K an odd number of
+        // 128-blocks); its partial is zero and it is folded with scale 0.
+        const float s_lo = g[0].s[0];
+        const float s_hi = 2 * seg + 1 < kbl ? g[0].s[1] : 0.f;
 #pragma unroll
         for (int d = 0; d + 1 < D; ++d)
             g[d] = g[d + 1];
         if (seg + D < s_end)
             load(g[D - 1], seg + D);
+        f32x4 p[2][T];      // partials of the segment's two K blocks (BS)
 #pragma unroll
         for (int u = 0; u < GV_SEG / 64; ++u) {
             const uint16_t *xp = &sx[wave][col * GV_XPITCH + 64 * u + 16 * grp];
@@ -293,11 +390,44 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
                     &sw[wave][(16 * t + col) * GV_WPITCH + 64 * u + 16 * grp]);
                 bf16x8 blo, bhi;
                 fp8x16_to_bf16(wv, blo, bhi);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
+                if constexpr (BS) {
+                    f32x4 &pb = p[u / 2][t];
+                    if (u % 2 == 0)
+                        pb = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, pb, 0, 0, 0);
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, pb, 0, 0, 0);
+                } else {
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
+                }
+            }
+            if constexpr (BS) {
+                // Folds trail the MFMAs that produce them by one K step, so
+                // the MFMA results are not waited for: the previous
+                // segment's second block after this segment's first step,
+                // this segment's first block after its third step.  The
+                // order of the additions is still block by block along K.
+                if (u == 0)
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        fold_block(acc[t], s_pend, p_pend[t]);
+                if (u == 2)
+#pragma unroll
+                    for (int t = 0; t < T; ++t)
+                        fold_block(acc[t], s_lo, p[0][t]);
             }
         }
+        if constexpr (BS) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                p_pend[t] = p[1][t];
+            s_pend = s_hi;
+        }
     }
+    if constexpr (BS)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+            fold_block(acc[t], s_pend, p_pend[t]);
 
     // Fixed-order reduction of the four K-quarter partial tiles.
     if (wave > 0) {
@@ -315,36 +445,37 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
             acc[t] += red[v][t][lane];
         uint32_t nn = row0 + 16u * t + col;
         if (nn < n) {
-            float sc = rs[nn];
+            float sc = BS ? 1.0f : rs[nn];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t mm = 4u * grp + i;
                 if (mm < m)
-                    out[(size_t)mm * n + nn] = (uint16_t)f32_to_bf16(acc[t][i] * sc);
+                    out[(size_t)mm * n + nn] =
+                        (uint16_t)f32_to_bf16(BS ? acc[t][i] : acc[t][i] * sc);
             }
         }
     }
 }
 
-template <int T, int D>
+template <int T, int D, bool BS>
 static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float *rs,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                                hipStream_t st)
 {
     constexpr uint32_t rows_wg = 16 * T;
     uint32_t grid = (n + rows_wg - 1) / rows_wg;
-    hipLaunchKernelGGL((k_fp8_gemv_ksplit<T, D>), dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_fp8_gemv_ksplit<T, D, BS>), dim3(grid), dim3(256), 0, st,
                        x, w, rs, out, m, n, k);
 }
 
-template <int T, int D>
+template <int T, int D, bool BS>
 static void launch_gemv_rows(const uint16_t *x, const uint8_t *w, const float *rs,
                              uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                              hipStream_t st)
 {
     constexpr uint32_t rows_wg = 64 * T;
     uint32_t grid = (n + rows_wg - 1) / rows_wg;
-    hipLaunchKernelGGL((k_fp8_gemv_rows<T, D>), dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_fp8_gemv_rows<T, D, BS>), dim3(grid), dim3(256), 0, st,
                        x, w, rs, out, m, n, k);
 }
 
@@ -359,9 +490,22 @@ hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
                                     uint32_t n, uint32_t k, hipStream_t st)
 {
     if (gemv_wide(n))
-        launch_gemv_rows<2, 1>(x, w, rs, out, m, n, k, st);
+        launch_gemv_rows<2, 1, false>(x, w, rs, out, m, n, k, st);
     else
-        launch_gemv_ksplit<1, 1>(x, w, rs, out, m, n, k, st);
+        launch_gemv_ksplit<1, 1, false>(x, w, rs, out, m, n, k, st);
+    count_launch();
+    return hipGetLastError();
+}
+
+// n % 128 == 0 and k % 128 == 0 (checked by the caller).
+hipError_t launch_fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
+                                      const float *grid, uint16_t *out, uint32_t m,
+                                      uint32_t n, uint32_t k, hipStream_t st)
+{
+    if (gemv_wide(n))
+        launch_gemv_rows<2, 1, true>(x, w, grid, out, m, n, k, st);
+    else
+        launch_gemv_ksplit<1, 1, true>(x, w, grid, out, m, n, k, st);
     count_launch();
     return hipGetLastError();
 }

@@ -216,6 +216,25 @@ int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
                       uint32_t n, uint32_t k, void *stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_gemv_blockscale -- block-scaled FP8-weight GEMV for decode and verify
+ * batches (fp8_gemv_batch.rs, w8a16_gemv_batch4 / w8a16_gemv_batch2, the
+ * batched siblings of w8a16_gemv, which take the raw 2D block-scaled FP8
+ * weight):
+ *   C[i,j] = bf16( sum_t x[i,t] * e4m3(w[j,t]) * block_scale[j/128][t/128] ),
+ *   x [m,k] BF16, w [n,k] E4M3, block_scale [n/128, k/128] F32 row-major,
+ *   out [m,n] BF16; all device memory owned by the caller, out written.
+ * 1 <= m <= 16 (else QP_ERR_RANGE; the pages' batched kernels stop at 4);
+ * n % 128 == 0 and k % 128 == 0 (else QP_ERR_SHAPE).  Each 128-element K
+ * block is summed in F32 and added to the running F32 sum with one FMA by
+ * its scale; the BF16 rounding happens once at the end.  The weight is
+ * streamed once for all m rows, and every output row is bit-identical to the
+ * m == 1 call on that row.
+ * ---------------------------------------------------------------------- */
+int fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
+                        const float *block_scale, uint16_t *out, uint32_t m,
+                        uint32_t n, uint32_t k, void *stream);
+
+/* ------------------------------------------------------------------------
  * Library information.
  * ---------------------------------------------------------------------- */
 /* Number of kernel launches this process has enqueued through the library

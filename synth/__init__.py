@@ -119,6 +119,17 @@ def gemv_acts_bf16(m: int, k: int, device="cpu", shape_id: int = 0) -> torch.Ten
     return bf16_normal((m, k), 1.0, seed_of(1, 2 * shape_id + 1), device)
 
 
+def gemv_block_weight(n: int, k: int, device="cpu", shape_id: int = 0):
+    """Block-scaled FP8 decode weight: E4M3 codes of a N(0,1) draw times 64
+    (most of the E4M3 range, no saturation) and an F32 grid [N/128, K/128]
+    of 128 x 128 block scales log-uniform in [1e-4, 1e-2]."""
+    case = 5
+    z = normal_f32((n, k), 1.0, seed_of(case, 2 * shape_id), device)
+    w = e4m3_bytes_of((z * 64.0).clamp(-448.0, 448.0))
+    grid = loguniform((n // 128, k // 128), 1e-4, 1e-2, seed_of(case, 2 * shape_id + 1), device)
+    return w, grid
+
+
 @dataclass
 class W4A8Prefill:
     w_bf16: torch.Tensor

@@ -49,8 +49,12 @@ def assert_gemm_close(got_bits, ref_bits, what=""):
 
 
 def assert_gemv_close(got_bits, ref_bits, what=""):
-    """Row-scaled GEMV bound: 2 BF16 ulp of |C_ref|, with a floor of
-    2^-14 * rms(C_ref[m, :]) for outputs near zero."""
+    """FP8 GEMV bound (row- or block-scaled): 2 BF16 ulp of |C_ref|, with a
+    floor of 2^-14 * rms(C_ref[m, :]) for outputs near zero.  The kernels
+    form exact products and sum them in F32 (K <= 2^16 terms, F32 error
+    <= ~2^-24 * K * max term, far below the floor at these shapes); the one
+    BF16 rounding accounts for the first ulp, F32 summation-order effects
+    on a value next to a BF16 tie for the second."""
     g, r = bf16_f64(got_bits), bf16_f64(ref_bits)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-38))) - 7)

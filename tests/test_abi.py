@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     for n in ["requant_w_nvfp4_int8", "requant_a_bf16_int8", "int8_gemm_blockscaled",
               "quantize_bf16_nvfp4", "w4a4_gemm", "requant_w_blockfp8_rowwise",
               "fp8_gemv_rowscale", "quant_rowwise_fp8", "fp8_gemm_rowscale",
-              "int8_gemm_block_partials", "qproj_launch_count"]:
+              "int8_gemm_block_partials", "fp8_gemv_blockscale", "qproj_launch_count"]:
         assert n in names
 
 
@@ -69,6 +69,16 @@ def test_gemv_m_range_and_k_multiple():
     assert L.fp8_gemv_rowscale(FAKE, FAKE, FAKE, FAKE, 4, 0, 64, None) == qp.QP_ERR_SHAPE
     assert L.fp8_gemv_rowscale(None, FAKE, FAKE, FAKE, 4, 64, 64, None) == qp.QP_ERR_NULL
     assert L.fp8_gemv_rowscale(FAKE + 4, FAKE, FAKE, FAKE, 4, 64, 64, None) == qp.QP_ERR_ALIGN
+
+
+def test_block_scaled_gemv_needs_128_multiples():
+    # The scale grid covers whole 128 x 128 weight blocks.
+    for m in (0, 17):
+        assert L.fp8_gemv_blockscale(FAKE, FAKE, FAKE, FAKE, m, 128, 128, None) == qp.QP_ERR_RANGE
+    for n, k in ((64, 128), (128, 64), (200, 256), (256, 192), (0, 128), (128, 0)):
+        assert L.fp8_gemv_blockscale(FAKE, FAKE, FAKE, FAKE, 2, n, k, None) == qp.QP_ERR_SHAPE
+    assert L.fp8_gemv_blockscale(FAKE, FAKE, None, FAKE, 2, 128, 128, None) == qp.QP_ERR_NULL
+    assert L.fp8_gemv_blockscale(FAKE, FAKE, FAKE + 2, FAKE, 2, 128, 128, None) == qp.QP_ERR_ALIGN
 
 
 def test_int8_paths_need_k_multiple_of_32():

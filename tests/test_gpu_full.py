@@ -56,6 +56,33 @@ def test_gemv_decode_shapes(sid, n, k):
         assert torch.equal(o1.view(torch.int16), full16[i:i + 1].view(torch.int16))
 
 
+@pytest.mark.parametrize("sid,n,k", [(0, 6144, 5120), (1, 17408, 5120), (2, 152064, 5120)])
+def test_block_scaled_gemv_decode_shapes(sid, n, k):
+    """Block-scaled FP8 GEMV (w8a16_gemv_batch4 / _batch2) at the decode
+    shapes, M in {1, 2, 4}: E4M3 weight with 128 x 128 F32 block scales,
+    BF16 acts N(0,1).  Three whole 128-row blocks (the first, the last and
+    one drawn) are checked against the oracle, and every row of the M = 4
+    call against its single-row call."""
+    w, grid = synth.gemv_block_weight(n, k, DEV, shape_id=sid)
+    x = synth.gemv_acts_bf16(4, k, DEV, shape_id=sid)
+    nb = n // 128
+    blocks = sorted({0, nb - 1, int(np.random.default_rng(200 + sid).integers(1, nb - 1))})
+    wh, gh, xb = host(w), host(grid), bits(x)
+    for m in (1, 2, 4):
+        out = empty((m, n), torch.bfloat16)
+        qp.fp8_gemv_blockscale(x[:m], w, grid, out)
+        got = host(out)
+        for b in blocks:
+            ref = oracle.fp8_gemv_blockscale(xb[:m], np.ascontiguousarray(wh[128 * b:128 * (b + 1)]),
+                                             np.ascontiguousarray(gh[b:b + 1]))
+            assert_gemv_close(got[:, 128 * b:128 * (b + 1)], ref, f"N={n} M={m} block {b}")
+        if m == 4:
+            for i in range(4):
+                o1 = empty((1, n), torch.bfloat16)
+                qp.fp8_gemv_blockscale(x[i:i + 1], w, grid, o1)
+                assert torch.equal(o1.view(torch.int16), out[i:i + 1].view(torch.int16)), i
+
+
 def test_w4a8_prefill_full():
     """W4A8 prefill: NVFP4 weight 17408x5120 (from BF16 N(0,0.02), scale2 =
     max|W|/448) -> int8 per-32; BF16 acts 2048x5120 with 1% outliers x20."""

@@ -281,3 +281,56 @@ def test_fp8_gemv_wide_and_partial_segments(n, k):
         out = filled((m, n), torch.bfloat16)
         qp.fp8_gemv_rowscale(dev(x[:m].contiguous()), wq, ws, out)
         assert_gemv_close(host(out), oracle.fp8_gemv_rowscale(bits(x[:m]), ow, ows), f"gemv {n}x{k} m={m}")
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled FP8 GEMV (fp8_gemv_batch.rs, w8a16_gemv_batch4 / _batch2).
+@pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 1152), (6144, 5120),
+                                 (65664, 640)])
+def test_fp8_gemv_blockscale_all_m(n, k):
+    # k = 384 and 1152 end half-way through a 256-element segment; k = 1152
+    # leaves the last K-split wave without a segment; n = 65664 takes the
+    # row-split kernel.
+    w, grid = synth.gemv_block_weight(n, k, "cpu", shape_id=0)
+    x = synth.gemv_acts_bf16(16, k, "cpu", shape_id=3)
+    wd, gd = dev(w), dev(grid)
+    for m in (range(1, 17) if n * k < 6144 * 5120 else (1, 3, 16)):
+        out = filled((m, n), torch.bfloat16)
+        qp.fp8_gemv_blockscale(dev(x[:m].contiguous()), wd, gd, out)
+        assert_gemv_close(host(out), oracle.fp8_gemv_blockscale(bits(x[:m]), w.numpy(), grid.numpy()),
+                          f"block gemv {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("n,k", [(256, 512), (65536, 256)])
+def test_fp8_gemv_blockscale_every_code_and_extreme_scales(n, k):
+    # Every finite E4M3 code (subnormals included) appears in every row, and
+    # the grid mixes zero blocks with power-of-two scales from 2^-30 to 2^10.
+    g = np.random.default_rng(5)
+    w = g.integers(0, 256, (n, k), dtype=np.uint8)
+    w[:, :256] = np.arange(256, dtype=np.uint8)[None, :]
+    w[(w & 0x7F) == 0x7F] = 0x00
+    grid = np.exp2(g.integers(-30, 11, (n // 128, k // 128))).astype(np.float32)
+    grid[g.random(grid.shape) < 0.2] = 0.0
+    x = synth.gemv_acts_bf16(4, k, "cpu", shape_id=4)
+    out = filled((4, n), torch.bfloat16)
+    qp.fp8_gemv_blockscale(dev(x), dev(torch.from_numpy(w)), dev(torch.from_numpy(grid)), out)
+    assert_gemv_close(host(out), oracle.fp8_gemv_blockscale(bits(x), w, grid), "block gemv codes")
+
+
+@pytest.mark.parametrize("n,k", [(384, 640), (17408, 5120), (65536, 5120)])
+def test_fp8_gemv_blockscale_batched_rows_bit_identical_to_single_row(n, k):
+    """The pages' invariant for w8a16_gemv_batch4 (fp8_gemv_batch.rs): each
+    row of an M-row call equals, bit for bit, the single-row call."""
+    w, grid = synth.gemv_block_weight(n, k, "cpu", shape_id=1)
+    wd, gd = dev(w), dev(grid)
+    x = dev(synth.gemv_acts_bf16(16, k, "cpu", shape_id=5))
+    singles = []
+    for i in range(16):
+        o = empty((1, n), torch.bfloat16)
+        qp.fp8_gemv_blockscale(x[i:i + 1], wd, gd, o)
+        singles.append(o)
+    single = torch.cat(singles)
+    for m in (2, 4, 16):
+        o = empty((m, n), torch.bfloat16)
+        qp.fp8_gemv_blockscale(x[:m], wd, gd, o)
+        assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
