@@ -76,6 +76,7 @@ def lib():
         L.oracle_w4a4_gemm.argtypes = [P, P, P, P, P, F, F, I, I, I]
         L.oracle_fp8_gemv_rowscale.argtypes = [P, P, P, P, I, I, I]
         L.oracle_fp8_gemv_blockscale.argtypes = [P, P, P, P, I, I, I]
+        L.oracle_w4a16_gemv.argtypes = [P, P, P, F, P, I, I, I]
         L.oracle_fp8_gemm_rowscale.argtypes = [P, P, P, P, P, I, I, I]
         L.oracle_num_threads.restype = ctypes.c_int
         for fn in ("oracle_requant_a_bf16_int8", "oracle_requant_w_nvfp4_int8",
@@ -83,7 +84,8 @@ def lib():
                    "oracle_requant_w_blockfp8_rowwise",
                    "oracle_int8_block_partials", "oracle_int8_gemm_blockscaled",
                    "oracle_w4a4_gemm", "oracle_fp8_gemv_rowscale",
-                   "oracle_fp8_gemv_blockscale", "oracle_fp8_gemm_rowscale"):
+                   "oracle_fp8_gemv_blockscale", "oracle_w4a16_gemv",
+                   "oracle_fp8_gemm_rowscale"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -263,6 +265,20 @@ def fp8_gemv_blockscale(x_bf16, w, block_scale) -> np.ndarray:
     assert block_scale.shape == (n // 128, k // 128)
     out = np.empty((m, n), np.uint16)
     lib().oracle_fp8_gemv_blockscale(_p(x), _p(w), _p(block_scale), _p(out), m, n, k)
+    return out
+
+
+def w4a16_gemv(x_bf16, w_packed, w_scale, scale2) -> np.ndarray:
+    """BF16 [m,k] x NVFP4 (packed [n,k/2], E4M3 per-16 scales [n,k/16],
+    per-tensor scale2) -> BF16 bits [m,n]."""
+    x = _c(x_bf16, np.uint16)
+    wp = _c(w_packed, np.uint8)
+    ws = _c(w_scale, np.uint8)
+    m, k = x.shape
+    n = wp.shape[0]
+    assert k % 16 == 0 and wp.shape == (n, k // 2) and ws.shape == (n, k // 16)
+    out = np.empty((m, n), np.uint16)
+    lib().oracle_w4a16_gemv(_p(x), _p(wp), _p(ws), float(scale2), _p(out), m, n, k)
     return out
 
 

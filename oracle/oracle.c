@@ -427,6 +427,33 @@ void oracle_fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
         }
 }
 
+/* fp8_gemv_batch.rs names w4a16_gemv_batch8_rt2 as the NVFP4-weight twin of
+ * the row-scaled FP8 GEMV.  BF16 x [m,k] times an NVFP4 weight: E2M1 codes
+ * packed [n,k/2] (element 2j in the low nibble of byte j), an E4M3 scale per
+ * 16 elements [n,k/16] and the per-tensor F32 scale2 (value = e2m1 * e4m3 *
+ * scale2, as for gemm_fp4.rs, quantize_bf16_to_nvfp4):
+ *   C[i,j] = bf16( scale2 * sum_t x[i,t] * e2m1(w[j,t]) * e4m3(s[j,t/16]) ).
+ * Each product is exact in binary64 (8 + 2 + 4 significant bits); the sum
+ * and the final scale2 product are binary64, and BF16 rounding happens once. */
+void oracle_w4a16_gemv(const uint16_t *x, const uint8_t *wp, const uint8_t *ws,
+                       float scale2, uint16_t *out,
+                       int64_t m, int64_t n, int64_t k)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t j = 0; j < n; ++j)
+        for (int64_t i = 0; i < m; ++i) {
+            double c = 0.0;
+            for (int64_t t = 0; t < k; ++t) {
+                uint8_t b = wp[j * (k / 2) + t / 2];
+                uint8_t code = (t % 2 == 0) ? (uint8_t)(b & 15) : (uint8_t)(b >> 4);
+                c += (double)oracle_bf16_to_float(x[i * k + t]) *
+                     oracle_e2m1_decode(code) *
+                     oracle_e4m3_decode(ws[j * (k / 16) + t / 16]);
+            }
+            out[i * n + j] = oracle_bf16_from_double((double)scale2 * c);
+        }
+}
+
 /* dispatch_proj_rowwise.rs, cublas_fp8_rowwise_proj (the row-wise FP8 GEMM
  * it ends in): C = bf16(sa[m] * sw[n] * sum_k e4m3(a[m,k]) * e4m3(w[n,k])). */
 void oracle_fp8_gemm_rowscale(const uint8_t *a, const float *sa,

@@ -432,3 +432,87 @@ def test_fp8_gemv_blockscale_batched_rows_equal_single_row_calls():
     full = oracle.fp8_gemv_blockscale(x, w, s)
     for i in range(4):
         assert np.array_equal(full[i:i + 1], oracle.fp8_gemv_blockscale(x[i:i + 1], w, s))
+
+
+# ---------------------------------------------------------------------------
+# NVFP4-weight GEMV (W4A16; fp8_gemv_batch.rs names w4a16_gemv_batch8_rt2):
+# C[i,j] = bf16(scale2 * sum_t x[i,t] * e2m1(w[j,t]) * e4m3(s[j,t/16])).
+def _e2m1_ocp(code: int) -> Fraction:
+    """OCP MX FP4 (E2M1) from its bit fields: sign, 2-bit exponent (bias 1),
+    1-bit mantissa; exponent 0 is subnormal (0 or 0.5)."""
+    sign = -1 if code & 8 else 1
+    e, mb = (code >> 1) & 3, code & 1
+    mag = Fraction(mb, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(mb, 2))
+    return sign * mag
+
+
+def _e4m3_torch(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def _w4a16_case(seed, m, n, k):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.standard_normal(m * k)).reshape(m, k)
+    wp = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    # E4M3 block scales over subnormal and normal codes, no NaN
+    ws = rng.integers(0x01, 0x7F, (n, k // 16), dtype=np.uint8)
+    return x, wp, ws
+
+
+def test_w4a16_gemv_rational():
+    x, wp, ws = _w4a16_case(31, 2, 3, 64)
+    ws[0, 0], ws[1, 1], ws[2, 2] = 0x01, 0x07, 0x7E     # 2^-9, subnormal max, 448
+    scale2 = np.float32(0.37)
+    c = oracle.w4a16_gemv(x, wp, ws, scale2)
+    xf = oracle.bf16_bits_to_f32(x).astype(np.float64)
+    sf = _e4m3_torch(ws)
+    for i in range(2):
+        for j in range(3):
+            tot = Fraction(0)
+            for t in range(64):
+                code = (wp[j, t // 2] >> (4 * (t % 2))) & 15
+                tot += Fraction(float(xf[i, t])) * _e2m1_ocp(int(code)) * Fraction(float(sf[j, t // 16]))
+            assert c[i, j] == _bf16_exact(Fraction(float(scale2)) * tot), (i, j)
+
+
+def test_w4a16_gemv_unit_scales_is_bf16_of_f64_matmul():
+    # E4M3 code 0x38 is 1.0; with scale2 = 1 the GEMV is x @ e2m1(W)^T, which
+    # numpy's f64 matmul forms exactly here (sums of bf16 x small halves), so
+    # only the single BF16 rounding differs, at most on a tie.
+    x, wp, _ = _w4a16_case(32, 4, 16, 256)
+    ws = np.full((16, 256 // 16), 0x38, np.uint8)
+    c = oracle.w4a16_gemv(x, wp, ws, 1.0).astype(np.int64)
+    lo = np.vectorize(lambda b: float(_e2m1_ocp(int(b) & 15)))(wp)
+    hi = np.vectorize(lambda b: float(_e2m1_ocp(int(b) >> 4)))(wp)
+    wf = np.stack([lo, hi], axis=2).reshape(16, 256)
+    ref = oracle.bf16_bits_to_f32(x).astype(np.float64) @ wf.T
+    ref_bits = np.array([[_bf16_exact(Fraction(float(v))) for v in row] for row in ref], np.int64)
+    assert np.array_equal(c, ref_bits)
+
+
+def test_w4a16_gemv_nibble_order_and_block_indexing():
+    # A weight with one nonzero code picks exactly one activation column:
+    # element t sits in byte t/2 (low nibble for even t) and takes the scale
+    # of block t/16.
+    rng = np.random.default_rng(33)
+    m, k = 3, 64
+    x = _bf16(rng.standard_normal(m * k)).reshape(m, k)
+    xf = oracle.bf16_bits_to_f32(x).astype(np.float64)
+    ws = np.array([[0x30, 0x38, 0x40, 0x48]], np.uint8)          # 0.5, 1, 2, 4
+    sf = _e4m3_torch(ws)[0]
+    for t, code in [(0, 0x3), (1, 0xD), (17, 0x7), (46, 0x5), (63, 0xA)]:
+        wp = np.zeros((1, k // 2), np.uint8)
+        wp[0, t // 2] = code << (4 * (t % 2))
+        c = oracle.w4a16_gemv(x, wp, ws, 1.5)
+        for i in range(m):
+            want = Fraction(3, 2) * Fraction(float(xf[i, t])) * _e2m1_ocp(code) * \
+                Fraction(float(sf[t // 16]))
+            assert c[i, 0] == _bf16_exact(want), (t, i)
+
+
+def test_w4a16_gemv_batched_rows_equal_single_row_calls():
+    x, wp, ws = _w4a16_case(34, 4, 8, 128)
+    full = oracle.w4a16_gemv(x, wp, ws, 0.01)
+    for i in range(4):
+        assert np.array_equal(full[i:i + 1], oracle.w4a16_gemv(x[i:i + 1], wp, ws, 0.01))
