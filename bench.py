@@ -18,8 +18,9 @@ The same line carries:
   secondary     every other row of the hot path at its own workload size:
                 quantizers / requantizers in GB/s against HBM, the three
                 GEMMs in TFLOP/s against the MFMA peak of their data type,
-                and the block-scaled FP8 GEMV (128 x 128 F32 block scales)
-                at the decode shapes for M in {1, 2, 4}, in GB/s.
+                the block-scaled FP8 GEMV (128 x 128 F32 block scales)
+                at the decode shapes for M in {1, 2, 4}, and the NVFP4-weight
+                GEMV (W4A16) there for M in {1, 2, 8}, in GB/s.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
 """
@@ -332,6 +333,39 @@ def run_secondary(qp, synth, dev, only):
             del w, grid, copies, x
             torch.cuda.empty_cache()
         res["fp8_gemv_blockscale"] = rows
+
+    # NVFP4-weight GEMV (W4A16) at the decode shapes, M in {1, 2, 8}; the
+    # weight is a BF16 N(0,0.02) draw quantised by quantize_bf16_nvfp4.
+    if want("w4a16_gemv"):
+        rows = []
+        for sid, (n, k) in enumerate(GEMV_SHAPES):
+            wb = synth.gemv_weight_bf16(n, k, dev, shape_id=sid)
+            s2 = synth.per_tensor_scale2(wb)
+            wp = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+            ws = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+            qp.quantize_bf16_nvfp4(wb, wp, ws, s2)
+            del wb
+            wbytes = n * k // 2 + n * k // 16
+            copies = [(wp, ws)] + [(wp.clone(), ws.clone())
+                                   for _ in range(rot_count(wbytes) - 1)]
+            x = synth.gemv_acts_bf16(8, k, dev, shape_id=sid)
+            for m in (1, 2, 8):
+                o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                xm = x[:m]
+                ms = time_launches(lambda i: qp.w4a16_gemv(
+                    xm, copies[i % len(copies)][0], copies[i % len(copies)][1], s2, o),
+                    iters=max(20, 2 * len(copies)))
+                abytes = wbytes + 2 * m * k + 2 * m * n
+                gbs = abytes / (ms * 1e-3) / 1e9
+                rows.append({"n": n, "k": k, "m": m, "us": round(ms * 1e3, 2),
+                             "weight_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                             "algorithmic_GBs": round(gbs, 1),
+                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+                log(f"  w4a16_gemv N={n} M={m}: {ms*1e3:.2f} us  "
+                    f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM)")
+            del wp, ws, copies, x
+            torch.cuda.empty_cache()
+        res["w4a16_gemv"] = rows
 
     # W4A8 prefill: NVFP4 weight 17408x5120 -> int8; acts 2048x5120.
     if want("w4a8") or want("requant_a_bf16_int8") or want("requant_w_nvfp4_int8") \

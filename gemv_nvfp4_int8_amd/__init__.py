@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "fp8_rowwise_proj": [I, P, P, P, P, P, P, P, P, U, U, U, P],
             "fp8_gemv_rowscale": [P, P, P, P, U, U, U, P],
             "fp8_gemv_blockscale": [P, P, P, P, U, U, U, P],
+            "w4a16_gemv": [P, P, P, F, P, U, U, U, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -311,11 +312,23 @@ def fp8_gemv_blockscale(x, w, block_scale, out, stream=None):
         _ptr(x), _ptr(w), _ptr(block_scale), _ptr(out), m, n, k, _stream(stream)))
 
 
+def w4a16_gemv(x, w_packed, w_e4m3, scale2, out, stream=None):
+    m, k = x.shape
+    n = w_packed.shape[0]
+    _need(x, "x", BF16, (m, k))
+    _need(w_packed, "w_packed", U8, (n, k // 2))
+    _need(w_e4m3, "w_e4m3", U8, (n, k // 16))
+    _need(out, "out", BF16, (m, n))
+    _check("w4a16_gemv", lib().w4a16_gemv(
+        _ptr(x), _ptr(w_packed), _ptr(w_e4m3), float(scale2), _ptr(out), m, n, k,
+        _stream(stream)))
+
+
 __all__ = [
     "requant_w_nvfp4_int8", "requant_a_bf16_int8", "int8_gemm_blockscaled",
     "int8_w4a8_prefill", "int8_gemm_block_partials", "quantize_bf16_nvfp4",
     "w4a4_gemm", "requant_w_blockfp8_rowwise", "quant_rowwise_fp8",
     "fp8_gemm_rowscale", "fp8_rowwise_proj", "fp8_gemv_rowscale",
-    "fp8_gemv_blockscale",
+    "fp8_gemv_blockscale", "w4a16_gemv",
     "launch_count", "status_string", "abi_version", "lib", "QProjError",
 ]

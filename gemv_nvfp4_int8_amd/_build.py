@@ -9,6 +9,12 @@ the source tree.  Flags:
   -fhip-fp32-correctly-rounded-divide-sqrt  IEEE binary32 division, which the
                                          code rounding relies on
   -target-feature -packed-fp32-ops       no packed-FP32 VALU instructions
+Per file (FILE_FLAGS):
+  gemv_w4a16.hip: -mllvm -amdgpu-mfma-vgpr-form   MFMA results in ordinary
+                                         VGPRs: its kernels fold every MFMA
+                                         result with VALU FMAs, and the
+                                         accumulator-register form costs a
+                                         copy per value read
 """
 from __future__ import annotations
 
@@ -34,13 +40,18 @@ DEVICE_FLAGS = [
 ]
 
 
+FILE_FLAGS = {
+    "gemv_w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -266,4 +266,19 @@ int fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
     return done(qp::launch_fp8_gemv_blockscale(x, w, block_scale, out, m, n, k, S(stream)));
 }
 
+int w4a16_gemv(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3,
+               float scale2, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+               void *stream)
+{
+    if (int e = check_ptrs({x, w_packed, w_e4m3, out}))
+        return e;
+    if (m < 1 || m > 8)
+        return QP_ERR_RANGE;
+    // (the kernel addresses every buffer with 30-bit offsets)
+    if (n == 0 || k == 0 || k % 32 != 0 || !fits(n, k) || !fits(m, n) ||
+        (uint64_t)m * k * 2 >= (1u << 30))
+        return QP_ERR_SHAPE;
+    return done(qp::launch_w4a16_gemv(x, w_packed, w_e4m3, scale2, out, m, n, k, S(stream)));
+}
+
 } // extern "C"

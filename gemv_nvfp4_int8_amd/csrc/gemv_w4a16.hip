@@ -1,0 +1,508 @@
+// gemv_w4a16.hip -- NVFP4-weight GEMV (W4A16) for decode / verify batches
+// (M <= 8) on gfx950 (fp8_gemv_batch.rs names w4a16_gemv_batch8_rt2 as the
+// NVFP4-weight twin of the register-tiled row-scaled FP8 GEMV).
+//
+//   C[i,j] = bf16( scale2 * sum_t x[i,t] * e2m1(w[j,t]) * e4m3(s[j,t/16]) )
+//
+// x [M,K] BF16; the weight is E2M1 codes packed [N,K/2] (element 2t in the
+// low nibble of byte t) with one E4M3 scale per 16 elements [N,K/16] and a
+// per-tensor F32 scale2.
+//
+// Design (MI355X-first):
+//  * The contraction runs on v_mfma_f32_4x4x4_16b_bf16: 16 independent
+//    4x4x4 blocks per instruction.  Here the 16 blocks are 16 K-slices of the
+//    same 4 weight rows and 4 activation rows, so one MFMA covers 64 K
+//    elements, and the block results are summed once at the end (a fixed
+//    butterfly over lanes).  Lane l supplies column l%4 of block l/4 of the
+//    weight operand and row l%4 of block l/4 of the activation operand, and
+//    receives column l%4 of block l/4 of the result: all four of its results
+//    belong to one weight row.
+//  * Dequantisation by folding the scale.  A lane's 32 consecutive elements
+//    of one weight row are exactly two 16-element scale blocks.  The E2M1
+//    codes go to BF16 exactly with the hardware converter at unit scale;
+//    the 4 MFMAs of one block accumulate into a fresh F32 partial, which is
+//    added to the running sum with one FMA per result by the block's
+//    decoded E4M3 scale.  Per 32 weight elements a lane spends 16
+//    conversions, 2 scale decodes and 8 FMAs (the converters' own scale
+//    operand applies only the power-of-two part of a scale, and gfx950 has
+//    no packed BF16 multiply, so scaling each element would cost twice
+//    that).  scale2 multiplies the F32 sum at write-out.
+//  * That layout also lets one 64-lane load feed the MFMAs directly: lane l
+//    loads 16 bytes (32 elements) of weight row l%4 at byte 16 (l/4) of a
+//    256-byte window, so every load instruction covers 4 rows x 256
+//    contiguous bytes -- the burst HBM serves best -- and the weights need
+//    no LDS transpose.  A lane needs 2 scale bytes per window; with wide
+//    weights the workgroup stages whole 128-byte scale lines (4 windows of
+//    a row) in LDS, with narrow ones each lane loads its 2 bytes.
+//  * Activations: for each 512-element window, lane l uses 32 elements of
+//    activation row 4g + l%4 (M group g) for every weight row group of the
+//    wave.  With wide weights the four waves of a workgroup stage the window
+//    in LDS once (double-buffered, one barrier per window) instead of each
+//    fetching it from L2.
+//  * Two register stages are used in turn, so each wave keeps the next two
+//    windows in flight.  Every load is a raw buffer load: a lane whose data
+//    does not exist (rows >= n or >= m, K past the end, a prefetch past the
+//    last window) gets an offset beyond the buffer and reads zero without
+//    touching memory, so no load sits under a branch.
+//  * Work split from N alone: wide weights give each wave its own rows over
+//    all of K; narrow weights split the windows of 8 rows over the four
+//    waves of a workgroup and add the partial sums in a fixed order.  No
+//    summation order depends on M, so every output row is bit-identical to
+//    an M = 1 call on that row.
+#include "qp_device.hpp"
+#include "qp_launch.hpp"
+
+namespace qp {
+
+constexpr int W4_WIN = 512;                 // K elements per window
+constexpr int W4_WB = W4_WIN / 2;           // packed bytes per row per window
+constexpr int W4_SB = W4_WIN / 16;          // scale bytes per row per window
+
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// Offsets >= W4_OOB lie beyond every buffer (each is < 2^30 bytes, checked
+// by the caller); a base offset plus a window offset, either possibly
+// W4_OOB, stays below 2^31.
+constexpr uint32_t W4_OOB = 1u << 30;
+constexpr int W4_NT = 2;                    // cache policy: nontemporal
+
+__device__ __forceinline__ buf_rsrc make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Four E2M1 codes (bytes SEL, SEL+1 of w; low nibble first) as BF16, exact.
+template <int SEL>
+__device__ __forceinline__ s16x4 fp4x4_bf16(uint32_t w)
+{
+    bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+    bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL + 1);
+    return __builtin_bit_cast(s16x4, (u32x2){__builtin_bit_cast(uint32_t, lo),
+                                             __builtin_bit_cast(uint32_t, hi)});
+}
+
+// Activation fragments of one window: 32 BF16 of row 4 g + l%4 per group.
+template <int MG>
+struct W4Act {
+    u32x4 x[MG][4];
+};
+
+// One window's weights in registers (RG groups of 4 rows).
+template <int RG>
+struct W4Wts {
+    u32x4 w[RG];            // 32 codes of weight row 4 rg + l%4
+    uint32_t s[RG];         // its two block scales (low 16 bits)
+};
+
+// Per-lane load offsets at window 0 of one wave (rows row0 .. row0 + 4 RG - 1).
+//   weights: lane l -> row 4 rg + l%4, bytes 16 (l/4) .. of the 256-byte window
+//   scales:  the same row, bytes 2 (l/4), +1 of the 32-byte window
+//   direct activation fragments (K split): row 4 g + l%4, elements
+//            32 (l/4) .. +31 of the 512-element window
+template <int MG, int RG>
+struct W4Src {
+    buf_rsrc rw, rs, rx;
+    uint32_t wo[RG], so[RG], xo[MG];
+    uint32_t kc;            // K index of the lane's chunk within a window
+
+    __device__ __forceinline__ void init(const uint16_t *x, const uint8_t *wp, const uint8_t *ws,
+                                         uint32_t row0, uint32_t m, uint32_t n, uint32_t k,
+                                         int lane)
+    {
+        rw = make_rsrc(wp, n * (k / 2));
+        rs = make_rsrc(ws, n * (k / 16));
+        rx = make_rsrc(x, m * k * 2);
+        kc = 32 * (lane / 4);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            uint32_t r = row0 + 4 * rg + lane % 4;
+            wo[rg] = r < n ? r * (k / 2) + kc / 2 : W4_OOB;
+            so[rg] = r < n ? r * (k / 16) + kc / 16 : W4_OOB;
+        }
+#pragma unroll
+        for (int g = 0; g < MG; ++g) {
+            uint32_t r = 4 * g + lane % 4;
+            xo[g] = r < m ? (r * k + kc) * 2 : W4_OOB;
+        }
+    }
+    // Window `win`; lanes whose 32-element chunk lies past K (or every lane,
+    // when ok is false) read zero.  SC: also load the lane's scale bytes.
+    template <bool SC = true>
+    __device__ __forceinline__ void load_w(W4Wts<RG> &g, uint32_t win, bool ok, uint32_t k) const
+    {
+        bool in = ok && win * W4_WIN + kc < k;
+        uint32_t dw = in ? win * W4_WB : W4_OOB, ds = in ? win * W4_SB : W4_OOB;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+            g.w[rg] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo[rg] + dw, 0, W4_NT);
+        if constexpr (SC) {
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+                g.s[rg] = __builtin_amdgcn_raw_buffer_load_b16(rs, so[rg] + ds, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void load_x(W4Act<MG> &a, uint32_t win, bool ok, uint32_t k) const
+    {
+        bool in = ok && win * W4_WIN + kc < k;
+        uint32_t dx = in ? win * W4_WIN * 2 : W4_OOB;
+#pragma unroll
+        for (int g = 0; g < MG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.x[g][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo[g] + dx + 16 * i, 0, 0);
+    }
+};
+
+// One 16-element scale block (half H of the lane's chunk) of row group rg:
+// 4 MFMAs into a fresh partial per M group, then acc += scale * partial.
+template <int MG, int RG, int H>
+__device__ __forceinline__ void w4_block(f32x4 *acc, const W4Wts<RG> &w, const W4Act<MG> &a, int rg)
+{
+    const float s = __builtin_amdgcn_cvt_f32_fp8((int)w.s[rg], H);
+    s16x4 b[4];
+    b[0] = fp4x4_bf16<0>(w.w[rg][2 * H]);
+    b[1] = fp4x4_bf16<2>(w.w[rg][2 * H]);
+    b[2] = fp4x4_bf16<0>(w.w[rg][2 * H + 1]);
+    b[3] = fp4x4_bf16<2>(w.w[rg][2 * H + 1]);
+    f32x4 p[MG];
+#pragma unroll
+    for (int g = 0; g < MG; ++g)
+        p[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * H + i;        // activation elements 4e .. 4e+3 of the chunk
+#pragma unroll
+        for (int g = 0; g < MG; ++g) {
+            u32x2 xa = (u32x2){a.x[g][e / 2][2 * (e % 2)], a.x[g][e / 2][2 * (e % 2) + 1]};
+            p[g] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, xa), b[i],
+                                                          p[g], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            acc[g][q] = __builtin_fmaf(s, p[g][q], acc[g][q]);
+}
+
+template <int MG, int RG>
+__device__ __forceinline__ void w4_window(f32x4 (*acc)[MG], const W4Wts<RG> &w, const W4Act<MG> &a)
+{
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        w4_block<MG, RG, 0>(acc[rg], w, a, rg);
+        w4_block<MG, RG, 1>(acc[rg], w, a, rg);
+    }
+}
+
+// Sum the 16 block results (lanes with equal l%4) with a fixed butterfly;
+// lanes 0..3 end up with the totals.
+template <int MG, int RG>
+__device__ __forceinline__ void w4_block_sum(f32x4 (*acc)[MG])
+{
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int g = 0; g < MG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = acc[rg][g][i];
+                v += __shfl_xor(v, 4, WAVE);
+                v += __shfl_xor(v, 8, WAVE);
+                v += __shfl_xor(v, 16, WAVE);
+                v += __shfl_xor(v, 32, WAVE);
+                acc[rg][g][i] = v;
+            }
+}
+
+// Lanes 0..3: C[4g + i][row0 + 4rg + lane] = bf16(acc * scale2).
+template <int MG, int RG>
+__device__ __forceinline__ void w4_store(f32x4 (*acc)[MG], float scale2, uint16_t *out,
+                                         uint32_t row0, uint32_t m, uint32_t n, int lane)
+{
+    if (lane >= 4)
+        return;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        uint32_t nn = row0 + 4 * rg + lane;
+        if (nn >= n)
+            continue;
+#pragma unroll
+        for (int g = 0; g < MG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t mm = 4 * g + i;
+                if (mm < m)
+                    out[(size_t)mm * n + nn] = (uint16_t)f32_to_bf16(acc[rg][g][i] * scale2);
+            }
+    }
+}
+
+template <int MG, int RG>
+__device__ __forceinline__ void w4_zero(f32x4 (*acc)[MG])
+{
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int g = 0; g < MG; ++g)
+            acc[rg][g] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+// ---------------------------------------------------------------------------
+// Wide weights: each wave owns 4 RG rows over all of K.  The workgroup's four
+// waves stage each activation window [4 MG rows x 512] in LDS together
+// (thread t loads 16-byte chunks t, t + 256, ...), one barrier per window.
+// ---------------------------------------------------------------------------
+constexpr int W4_XPITCH = W4_WIN + 8;       // LDS bf16 per activation row
+constexpr int W4_GW = 2;                    // windows per scale group
+constexpr int W4_GB = W4_GW * W4_SB;        // scale bytes per row per group (64)
+
+// Wide weights, scales: the workgroup loads the scale bytes of all its rows
+// for a group of 2 windows (64 bytes per row, 8 bytes per thread) one group
+// ahead and keeps them in LDS (double-buffered), instead of each lane
+// fetching its own 2 bytes per window.
+template <int MG, int RG>
+__global__ __launch_bounds__(256) void k_w4a16_gemv_rows(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
+    const uint8_t *__restrict__ ws, float scale2, uint16_t *__restrict__ out,
+    uint32_t m, uint32_t n, uint32_t k)
+{
+    constexpr int ROWS = 4 * RG;
+    constexpr int WG_ROWS = 4 * ROWS;
+    constexpr int XC = MG;                  // activation chunks per thread and window
+    constexpr int SCH = (WG_ROWS * (W4_GB / 8) + 255) / 256;    // scale chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t sx[2][4 * MG * W4_XPITCH];
+    __shared__ __attribute__((aligned(16))) uint8_t ss[2][WG_ROWS * W4_GB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t wg_row0 = blockIdx.x * WG_ROWS;
+    const uint32_t row0 = wg_row0 + wave * ROWS;
+    const uint32_t nwin = (k + W4_WIN - 1) / W4_WIN;
+    const uint32_t srow = k / 16;           // scale bytes per row
+
+    W4Src<MG, RG> src;
+    src.init(x, wp, ws, row0, m, n, k, lane);
+    // staged activation chunk c = tid + 256 j: row c / 64, elements 8 (c % 64) ..
+    buf_rsrc rx = src.rx;
+    uint32_t xso[XC], xke[XC];
+    int xlo[XC];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+        int c = tid + 256 * j, r = c >> 6;
+        xke[j] = 8 * (c & 63);
+        xso[j] = (uint32_t)r < m ? (r * k + xke[j]) * 2 : W4_OOB;
+        xlo[j] = r * W4_XPITCH + xke[j];
+    }
+    auto load_xs = [&](u32x4 *v, uint32_t win, bool ok) {
+#pragma unroll
+        for (int j = 0; j < XC; ++j) {
+            uint32_t dx = ok && win * W4_WIN + xke[j] < k ? win * W4_WIN * 2 : W4_OOB;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xso[j] + dx, 0, 0);
+        }
+    };
+    // staged scale chunk c = tid + 256 j: workgroup row c / 8, bytes 8 (c % 8)
+    // of the row's 64-byte group segment; chunks beyond the rows (or, for
+    // a workgroup of one row group, beyond the 128 RG chunks) read zero.
+    buf_rsrc rs = src.rs;
+    uint32_t sso[SCH], sbo[SCH];
+    int slo[SCH];
+#pragma unroll
+    for (int j = 0; j < SCH; ++j) {
+        int c = tid + 256 * j, r = c >> 3;
+        sbo[j] = 8 * (c & 7);
+        uint32_t gr = wg_row0 + r;
+        sso[j] = (c < WG_ROWS * 8 && gr < n) ? gr * srow + sbo[j] : W4_OOB;
+        slo[j] = r * W4_GB + sbo[j];
+    }
+    // Scale bytes at or beyond k/16 in a row are zeroed in registers (an
+    // 8-byte piece can straddle the end of a row's scales when k % 128 != 0);
+    // a zero scale times a zero partial adds nothing.
+    auto load_sg = [&](u32x2 *v, uint32_t grp) {
+#pragma unroll
+        for (int j = 0; j < SCH; ++j) {
+            uint32_t o = grp * W4_GB + sbo[j];
+            v[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, sso[j] + (o < srow ? grp * W4_GB : W4_OOB),
+                                                        0, 0);
+            uint32_t valid = o < srow ? srow - o : 0;      // bytes of this piece inside the row
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                uint32_t keep = valid >= 4 * d + 4 ? 0xFFFFFFFFu
+                                : valid > 4 * d    ? 0x0000FFFFu   // valid is even
+                                                   : 0u;
+                v[j][d] &= keep;
+            }
+        }
+    };
+    auto stash_sg = [&](const u32x2 *v, int buf) {
+#pragma unroll
+        for (int j = 0; j < SCH; ++j)
+            if (tid + 256 * j < WG_ROWS * 8)
+                *reinterpret_cast<u32x2 *>(&ss[buf][slo[j]]) = v[j];
+    };
+    // a lane's fragments: row 4 g + l%4, elements 32 (l/4) + 8 i ..
+    auto read_frags = [&](W4Act<MG> &a, int buf) {
+#pragma unroll
+        for (int g = 0; g < MG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.x[g][i] = *reinterpret_cast<const u32x4 *>(
+                    &sx[buf][(4 * g + lane % 4) * W4_XPITCH + 32 * (lane / 4) + 8 * i]);
+    };
+    // the lane's two scale bytes of window `wig` (0 or 1) of the group in buffer sb
+    auto read_scales = [&](W4Wts<RG> &g, int sb, int wig) {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+            g.s[rg] = *reinterpret_cast<const uint16_t *>(
+                &ss[sb][(wave * ROWS + 4 * rg + lane % 4) * W4_GB + wig * W4_SB + 2 * (lane / 4)]);
+    };
+
+    f32x4 acc[RG][MG];
+    w4_zero<MG, RG>(acc);
+
+    W4Wts<RG> A, B;
+    u32x4 xa[XC], xb[XC];
+    u32x2 sg[SCH];
+    load_sg(sg, 0);
+    src.template load_w<false>(A, 0, nwin > 0, k);
+    load_xs(xa, 0, nwin > 0);
+    src.template load_w<false>(B, 1, nwin > 1, k);
+    load_xs(xb, 1, nwin > 1);
+    W4Act<MG> frag;
+
+    // One window: stage its activations, prefetch the window two ahead,
+    // synchronise, compute.
+    auto step = [&](W4Wts<RG> &W, u32x4 *xs, uint32_t w, int buf, int sb, int wig) {
+#pragma unroll
+        for (int j = 0; j < XC; ++j)
+            *reinterpret_cast<u32x4 *>(&sx[buf][xlo[j]]) = xs[j];
+        load_xs(xs, w + 2, w + 2 < nwin);
+        __syncthreads();
+        read_frags(frag, buf);
+        read_scales(W, sb, wig);
+        w4_window<MG, RG>(acc, W, frag);
+        src.template load_w<false>(W, w + 2, w + 2 < nwin, k);
+    };
+    uint32_t win = 0;
+    for (; win + 2 <= nwin; win += 2) {
+        const int sb = (win / 2) & 1;
+        stash_sg(sg, sb);
+        load_sg(sg, win / 2 + 1);
+        step(A, xa, win, 0, sb, 0);
+        step(B, xb, win + 1, 1, sb, 1);
+    }
+    if (win < nwin) {               // an odd last window, already in A
+        const int sb = (win / 2) & 1;
+        stash_sg(sg, sb);
+        step(A, xa, win, 0, sb, 0);
+    }
+    w4_block_sum<MG, RG>(acc);
+    w4_store<MG, RG>(acc, scale2, out, row0, m, n, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Narrow weights: the four waves of a workgroup share 4 RG rows and split the
+// K windows; each fetches its own activation fragments, and the partial
+// sums are added in a fixed order.
+// ---------------------------------------------------------------------------
+template <int MG, int RG>
+__global__ __launch_bounds__(256) void k_w4a16_gemv_ksplit(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
+    const uint8_t *__restrict__ ws, float scale2, uint16_t *__restrict__ out,
+    uint32_t m, uint32_t n, uint32_t k)
+{
+    constexpr int ROWS = 4 * RG;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t row0 = blockIdx.x * ROWS;
+    const uint32_t nwin = (k + W4_WIN - 1) / W4_WIN;
+    const uint32_t w_beg = nwin * wave / 4, w_end = nwin * (wave + 1) / 4;
+
+    W4Src<MG, RG> src;
+    src.init(x, wp, ws, row0, m, n, k, lane);
+
+    f32x4 acc[RG][MG];
+    w4_zero<MG, RG>(acc);
+
+    W4Wts<RG> A, B;
+    W4Act<MG> XA, XB;
+    src.load_w(A, w_beg, w_beg < w_end, k);
+    src.load_x(XA, w_beg, w_beg < w_end, k);
+    src.load_w(B, w_beg + 1, w_beg + 1 < w_end, k);
+    src.load_x(XB, w_beg + 1, w_beg + 1 < w_end, k);
+    uint32_t win = w_beg;
+    for (; win + 2 <= w_end; win += 2) {
+        w4_window<MG, RG>(acc, A, XA);
+        src.load_w(A, win + 2, win + 2 < w_end, k);
+        src.load_x(XA, win + 2, win + 2 < w_end, k);
+        w4_window<MG, RG>(acc, B, XB);
+        src.load_w(B, win + 3, win + 3 < w_end, k);
+        src.load_x(XB, win + 3, win + 3 < w_end, k);
+    }
+    if (win < w_end)                // an odd last window, already in A
+        w4_window<MG, RG>(acc, A, XA);
+
+    w4_block_sum<MG, RG>(acc);
+
+    // Fixed-order sum of the four K parts of each row group.
+    __shared__ f32x4 red[4][RG][MG][4];
+    if (lane < 4) {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int g = 0; g < MG; ++g)
+                red[wave][rg][g][lane] = acc[rg][g];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    if (lane < 4) {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+            for (int g = 0; g < MG; ++g)
+                acc[rg][g] = ((red[0][rg][g][lane] + red[1][rg][g][lane]) + red[2][rg][g][lane]) +
+                             red[3][rg][g][lane];
+    }
+    w4_store<MG, RG>(acc, scale2, out, row0, m, n, lane);
+}
+
+// Row groups per wave (8 weight rows) for one and two M groups: more rows
+// per wave cost registers faster than they save activation reads.
+constexpr int W4_RG1 = 2, W4_RG2 = 2;
+
+// Work-split choice from n alone (never m).
+static bool w4_gemv_wide(uint32_t n) { return n >= 65536u; }
+
+template <int MG, int RG>
+static void launch_w4(const uint16_t *x, const uint8_t *wp, const uint8_t *ws, float scale2,
+                      uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t st)
+{
+    constexpr uint32_t ROWS = 4 * RG;
+    if (w4_gemv_wide(n)) {
+        uint32_t grid = (n + 4 * ROWS - 1) / (4 * ROWS);
+        hipLaunchKernelGGL((k_w4a16_gemv_rows<MG, RG>), dim3(grid), dim3(256), 0, st,
+                           x, wp, ws, scale2, out, m, n, k);
+    } else {
+        uint32_t grid = (n + ROWS - 1) / ROWS;
+        hipLaunchKernelGGL((k_w4a16_gemv_ksplit<MG, RG>), dim3(grid), dim3(256), 0, st,
+                           x, wp, ws, scale2, out, m, n, k);
+    }
+}
+
+// 1 <= m <= 8, k % 32 == 0 and every buffer < 2^30 bytes (checked by the
+// caller).  M groups of 4 rows: the group count changes no summation order.
+hipError_t launch_w4a16_gemv(const uint16_t *x, const uint8_t *wp, const uint8_t *ws,
+                             float scale2, uint16_t *out, uint32_t m, uint32_t n,
+                             uint32_t k, hipStream_t st)
+{
+    if (m <= 4)
+        launch_w4<1, W4_RG1>(x, wp, ws, scale2, out, m, n, k, st);
+    else
+        launch_w4<2, W4_RG2>(x, wp, ws, scale2, out, m, n, k, st);
+    count_launch();
+    return hipGetLastError();
+}
+
+} // namespace qp

@@ -27,6 +27,9 @@ hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
 hipError_t launch_fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
                                       const float *grid, uint16_t *out, uint32_t m,
                                       uint32_t n, uint32_t k, hipStream_t st);
+hipError_t launch_w4a16_gemv(const uint16_t *x, const uint8_t *wp, const uint8_t *ws,
+                             float scale2, uint16_t *out, uint32_t m, uint32_t n,
+                             uint32_t k, hipStream_t st);
 hipError_t launch_int8_gemm(const int8_t *a, const int8_t *w, const float *as,
                             const float *ws, uint16_t *out, int32_t *partials,
                             uint32_t m, uint32_t n, uint32_t k, hipStream_t st);

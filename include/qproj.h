@@ -235,6 +235,28 @@ int fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
                         uint32_t n, uint32_t k, void *stream);
 
 /* ------------------------------------------------------------------------
+ * w4a16_gemv -- NVFP4-weight GEMV for decode and verify batches
+ * (fp8_gemv_batch.rs names w4a16_gemv_batch8_rt2 as the NVFP4 twin of the
+ * row-scaled FP8 GEMV):
+ *   C[i,j] = bf16( scale2 * sum_t x[i,t] * e2m1(w[j,t]) * e4m3(s[j,t/16]) ),
+ *   x        [m, k]    BF16
+ *   w_packed [n, k/2]  E2M1 codes, element 2t in the low nibble of byte t
+ *   w_e4m3   [n, k/16] E4M3 scale of each 16-element block
+ *   scale2             per-tensor F32 multiplier (value = e2m1*e4m3*scale2,
+ *                      the layout quantize_bf16_nvfp4 writes)
+ *   out      [m, n]    BF16, written
+ * All device memory owned by the caller.  1 <= m <= 8, the pages' batch
+ * (else QP_ERR_RANGE); k % 32 == 0 and 2*m*k < 2^30 (else QP_ERR_SHAPE).
+ * Each dequantised weight e2m1*e4m3 is exact in BF16; the products with x
+ * are exact and summed in F32; scale2 multiplies the F32 sum at write-out
+ * and BF16 rounding happens once.  The weight is streamed once for all m rows,
+ * and every output row is bit-identical to the m == 1 call on that row.
+ * ---------------------------------------------------------------------- */
+int w4a16_gemv(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3,
+               float scale2, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+               void *stream);
+
+/* ------------------------------------------------------------------------
  * Library information.
  * ---------------------------------------------------------------------- */
 /* Number of kernel launches this process has enqueued through the library

@@ -130,6 +130,16 @@ def gemv_block_weight(n: int, k: int, device="cpu", shape_id: int = 0):
     return w, grid
 
 
+def gemv_nvfp4_weight(n: int, k: int, device="cpu", shape_id: int = 0):
+    """NVFP4 decode weight drawn over every code: uniform random packed E2M1
+    bytes [N, K/2], E4M3 block scales = cast(|N(0,1)| * 0.05) [N, K/16]
+    (about a quarter subnormal, a few zero) and scale2 = 1/64."""
+    case = 6
+    wp = uniform_bytes((n, k // 2), seed_of(case, 2 * shape_id), device)
+    z = normal_f32((n, k // 16), 1.0, seed_of(case, 2 * shape_id + 1), device)
+    return wp, e4m3_bytes_of(z.abs() * 0.05), 1.0 / 64
+
+
 @dataclass
 class W4A8Prefill:
     w_bf16: torch.Tensor

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     for n in ["requant_w_nvfp4_int8", "requant_a_bf16_int8", "int8_gemm_blockscaled",
               "quantize_bf16_nvfp4", "w4a4_gemm", "requant_w_blockfp8_rowwise",
               "fp8_gemv_rowscale", "quant_rowwise_fp8", "fp8_gemm_rowscale",
-              "int8_gemm_block_partials", "fp8_gemv_blockscale", "qproj_launch_count"]:
+              "int8_gemm_block_partials", "fp8_gemv_blockscale", "w4a16_gemv",
+              "qproj_launch_count"]:
         assert n in names
 
 
@@ -79,6 +80,15 @@ def test_block_scaled_gemv_needs_128_multiples():
         assert L.fp8_gemv_blockscale(FAKE, FAKE, FAKE, FAKE, 2, n, k, None) == qp.QP_ERR_SHAPE
     assert L.fp8_gemv_blockscale(FAKE, FAKE, None, FAKE, 2, 128, 128, None) == qp.QP_ERR_NULL
     assert L.fp8_gemv_blockscale(FAKE, FAKE, FAKE + 2, FAKE, 2, 128, 128, None) == qp.QP_ERR_ALIGN
+
+
+def test_w4a16_gemv_argument_checks():
+    for m in (0, 9):
+        assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, m, 64, 64, None) == qp.QP_ERR_RANGE
+    for n, k in ((64, 16), (64, 48), (0, 64), (64, 0), (64, 1 << 27)):
+        assert L.w4a16_gemv(FAKE, FAKE, FAKE, 1.0, FAKE, 2, n, k, None) == qp.QP_ERR_SHAPE
+    assert L.w4a16_gemv(FAKE, None, FAKE, 1.0, FAKE, 2, 64, 64, None) == qp.QP_ERR_NULL
+    assert L.w4a16_gemv(FAKE, FAKE, FAKE + 4, 1.0, FAKE, 2, 64, 64, None) == qp.QP_ERR_ALIGN
 
 
 def test_int8_paths_need_k_multiple_of_32():

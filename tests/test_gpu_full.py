@@ -83,6 +83,34 @@ def test_block_scaled_gemv_decode_shapes(sid, n, k):
                 assert torch.equal(o1.view(torch.int16), out[i:i + 1].view(torch.int16)), i
 
 
+@pytest.mark.parametrize("sid,n,k", [(0, 6144, 5120), (1, 17408, 5120), (2, 152064, 5120)])
+def test_w4a16_gemv_decode_shapes(sid, n, k):
+    """NVFP4-weight GEMV at the decode shapes, M in {1, 2, 8}: the weight is
+    a BF16 N(0,0.02) draw quantised to NVFP4 by quantize_bf16_nvfp4 (scale2 =
+    max|W|/448), the acts BF16 N(0,1).  Sampled rows are checked against the
+    oracle on the same codes, and the M = 8 rows against single-row calls."""
+    wb = synth.gemv_weight_bf16(n, k, DEV, shape_id=sid)
+    s2 = synth.per_tensor_scale2(wb)
+    wp, ws = empty((n, k // 2), torch.uint8), empty((n, k // 16), torch.uint8)
+    qp.quantize_bf16_nvfp4(wb, wp, ws, s2)
+    del wb
+    x = synth.gemv_acts_bf16(8, k, DEV, shape_id=sid)
+    rows = _rows(n, 384, 300 + sid)
+    ridx = torch.from_numpy(rows).to(DEV)
+    owp, ows = host(wp.index_select(0, ridx)), host(ws.index_select(0, ridx))
+    xb = bits(x)
+    for m in (1, 2, 8):
+        out = empty((m, n), torch.bfloat16)
+        qp.w4a16_gemv(x[:m], wp, ws, s2, out)
+        got = host(out)[:, rows]
+        assert_gemv_close(got, oracle.w4a16_gemv(xb[:m], owp, ows, s2), f"N={n} M={m}")
+        if m == 8:
+            for i in (0, 7):
+                o1 = empty((1, n), torch.bfloat16)
+                qp.w4a16_gemv(x[i:i + 1], wp, ws, s2, o1)
+                assert torch.equal(o1.view(torch.int16), out[i:i + 1].view(torch.int16)), i
+
+
 def test_w4a8_prefill_full():
     """W4A8 prefill: NVFP4 weight 17408x5120 (from BF16 N(0,0.02), scale2 =
     max|W|/448) -> int8 per-32; BF16 acts 2048x5120 with 1% outliers x20."""

@@ -334,3 +334,60 @@ def test_fp8_gemv_blockscale_batched_rows_bit_identical_to_single_row(n, k):
         o = empty((m, n), torch.bfloat16)
         qp.fp8_gemv_blockscale(x[:m], wd, gd, o)
         assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
+
+
+# ---------------------------------------------------------------------------
+# NVFP4-weight GEMV, W4A16 (fp8_gemv_batch.rs names w4a16_gemv_batch8_rt2).
+@pytest.mark.parametrize("n,k", [(64, 64), (256, 96), (200, 352), (384, 1216), (6144, 5120),
+                                 (65600, 448), (65664, 1600)])
+def test_w4a16_gemv_all_m(n, k):
+    # k = 96 / 352 / 1216 / 448 / 1600 end 96 / 352 / 192 / 448 / 64
+    # elements into a 512-element window; k = 1216 (3 windows) leaves one
+    # K-split wave without a window; n >= 65536 takes the row-split kernel
+    # (ragged last tiles), whose staged scale pieces straddle the end of a
+    # row's scales at k = 448 and 1600.  m <= 4 and m > 4 take the one- and
+    # two-group kernels.
+    wp, ws, s2 = synth.gemv_nvfp4_weight(n, k, "cpu", shape_id=0)
+    x = synth.gemv_acts_bf16(8, k, "cpu", shape_id=6)
+    wpd, wsd = dev(wp), dev(ws)
+    for m in (range(1, 9) if n * k < 6144 * 5120 else (1, 3, 5, 8)):
+        out = filled((m, n), torch.bfloat16)
+        qp.w4a16_gemv(dev(x[:m].contiguous()), wpd, wsd, s2, out)
+        assert_gemv_close(host(out), oracle.w4a16_gemv(bits(x[:m]), wp.numpy(), ws.numpy(), s2),
+                          f"w4a16 {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("n,k", [(256, 512), (65536, 256)])
+def test_w4a16_gemv_every_code_and_scale(n, k):
+    # Every byte value (so every nibble pair) in every row, and every finite
+    # E4M3 scale code of either sign across the blocks.
+    g = np.random.default_rng(6)
+    wp = g.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    wp[:, :128] = np.arange(256, dtype=np.uint8)[:128][None, :] + \
+        (np.arange(n, dtype=np.uint8)[:, None] & 1) * 128
+    ws = g.integers(0, 256, (n, k // 16), dtype=np.uint8)
+    ws[(ws & 0x7F) == 0x7F] = 0x38
+    ws.reshape(-1)[:254] = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    x = synth.gemv_acts_bf16(4, k, "cpu", shape_id=7)
+    out = filled((4, n), torch.bfloat16)
+    qp.w4a16_gemv(dev(x), dev(torch.from_numpy(wp)), dev(torch.from_numpy(ws)), 0.75, out)
+    assert_gemv_close(host(out), oracle.w4a16_gemv(bits(x), wp, ws, 0.75), "w4a16 codes")
+
+
+@pytest.mark.parametrize("n,k", [(384, 640), (17408, 5120), (65536, 5120)])
+def test_w4a16_gemv_batched_rows_bit_identical_to_single_row(n, k):
+    """Each row of an M-row call equals, bit for bit, the single-row call
+    (the batched GEMV family's invariant, fp8_gemv_batch.rs)."""
+    wp, ws, s2 = synth.gemv_nvfp4_weight(n, k, "cpu", shape_id=1)
+    wpd, wsd = dev(wp), dev(ws)
+    x = dev(synth.gemv_acts_bf16(8, k, "cpu", shape_id=8))
+    singles = []
+    for i in range(8):
+        o = empty((1, n), torch.bfloat16)
+        qp.w4a16_gemv(x[i:i + 1], wpd, wsd, s2, o)
+        singles.append(o)
+    single = torch.cat(singles)
+    for m in (2, 4, 5, 8):
+        o = empty((m, n), torch.bfloat16)
+        qp.w4a16_gemv(x[:m], wpd, wsd, s2, o)
+        assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
