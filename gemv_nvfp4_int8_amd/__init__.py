@@ -28,6 +28,7 @@ QP_ERR_RANGE = -3
 QP_ERR_FORMAT = -4
 QP_ERR_HIP = -5
 QP_ERR_ALIGN = -6
+QP_ERR_ALLOC = -7
 
 QP_FP8_PER_ROW = 0
 QP_FP8_BLOCK128 = 1
@@ -72,6 +73,14 @@ def lib() -> ctypes.CDLL:
             "fp8_gemv_rowscale": [P, P, P, P, U, U, U, P],
             "fp8_gemv_blockscale": [P, P, P, P, U, U, U, P],
             "w4a16_gemv": [P, P, P, F, P, U, U, U, P],
+            "qproj_cache_create": [PP],
+            "qproj_cache_destroy": [P],
+            "qproj_cache_evict": [P, P],
+            "qproj_cache_stats": [P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)],
+            "requant_w_blockfp8_rowwise_cached": [P, I, P, P, U, U, PP, PP, P],
+            "requant_w_nvfp4_int8_cached": [P, P, P, F, U, U, PP, PP, P],
+            "fp8_rowwise_proj_cached": [P, I, P, P, P, P, P, P, U, U, U, P],
+            "int8_w4a8_prefill_cached": [P, P, P, P, F, P, P, P, U, U, U, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -324,11 +333,97 @@ def w4a16_gemv(x, w_packed, w_e4m3, scale2, out, stream=None):
         _stream(stream)))
 
 
+class DerivedWeights:
+    """A derived-weight cache (the library's qp_cache): weights requantised on
+    first use and kept, keyed by the source weight's device address
+    (dispatch_proj_rowwise.rs, requant_weight_rowwise_fp8_cached and its
+    DerivedWeights cache).  The cache owns the derived device buffers; the
+    requant methods return their device addresses as ints.  close() (or
+    garbage collection) frees them: no kernel reading one may be pending."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check("qproj_cache_create", lib().qproj_cache_create(ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().qproj_cache_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def stats(self):
+        """(entries, bytes) held by the cache."""
+        e, b = ctypes.c_uint64(), ctypes.c_uint64()
+        _check("qproj_cache_stats", lib().qproj_cache_stats(self._h, ctypes.byref(e), ctypes.byref(b)))
+        return int(e.value), int(b.value)
+
+    def evict(self, w):
+        _check("qproj_cache_evict", lib().qproj_cache_evict(self._h, _ptr(w)))
+
+    def requant_w_blockfp8_rowwise(self, fmt, w, scale, stream=None):
+        """Row-wise FP8 copy of a block-scaled weight (passthrough for
+        QP_FP8_PER_ROW): returns (weight address, scale address)."""
+        n, k = w.shape
+        _need(w, "w", U8, (n, k))
+        if fmt == QP_FP8_BLOCK128:
+            _need(scale, "scale", F32, (n // 128, k // 128))
+        wq, sq = ctypes.c_void_p(), ctypes.c_void_p()
+        _check("requant_w_blockfp8_rowwise_cached", lib().requant_w_blockfp8_rowwise_cached(
+            self._h, int(fmt), _ptr(w), _ptr(scale), n, k, ctypes.byref(wq), ctypes.byref(sq),
+            _stream(stream)))
+        return wq.value, sq.value
+
+    def requant_w_nvfp4_int8(self, w_packed, w_e4m3, scale2, stream=None):
+        """int8 copy [n,k] and F32 per-32 scales [n,k/32] of an NVFP4 weight:
+        returns (weight address, scale address)."""
+        n, kh = w_packed.shape
+        k = 2 * kh
+        _need(w_packed, "w_packed", U8, (n, k // 2))
+        _need(w_e4m3, "w_e4m3", U8, (n, k // 16))
+        wq, sq = ctypes.c_void_p(), ctypes.c_void_p()
+        _check("requant_w_nvfp4_int8_cached", lib().requant_w_nvfp4_int8_cached(
+            self._h, _ptr(w_packed), _ptr(w_e4m3), float(scale2), n, k, ctypes.byref(wq),
+            ctypes.byref(sq), _stream(stream)))
+        return wq.value, sq.value
+
+    def fp8_rowwise_proj(self, fmt, w, w_scale, act, act_q, act_scale, out, stream=None):
+        m, k = act.shape
+        n = w.shape[0]
+        _need(w, "w", U8, (n, k))
+        _need(w_scale, "w_scale", F32, (n,) if fmt == QP_FP8_PER_ROW else (n // 128, k // 128))
+        _need(act, "act", BF16, (m, k))
+        _need(act_q, "act_q", U8, (m, k))
+        _need(act_scale, "act_scale", F32, (m,))
+        _need(out, "out", BF16, (m, n))
+        _check("fp8_rowwise_proj_cached", lib().fp8_rowwise_proj_cached(
+            self._h, int(fmt), _ptr(w), _ptr(w_scale), _ptr(act), _ptr(act_q), _ptr(act_scale),
+            _ptr(out), m, n, k, _stream(stream)))
+
+    def int8_w4a8_prefill(self, a, w_packed, w_e4m3, scale2, a_i8, a_scale, out, stream=None):
+        m, k = a.shape
+        n = w_packed.shape[0]
+        _need(a, "a", BF16, (m, k))
+        _need(w_packed, "w_packed", U8, (n, k // 2))
+        _need(w_e4m3, "w_e4m3", U8, (n, k // 16))
+        _need(a_i8, "a_i8", I8, (m, k))
+        _need(a_scale, "a_scale", F32, (m, k // 32))
+        _need(out, "out", BF16, (m, n))
+        _check("int8_w4a8_prefill_cached", lib().int8_w4a8_prefill_cached(
+            self._h, _ptr(a), _ptr(w_packed), _ptr(w_e4m3), float(scale2), _ptr(a_i8),
+            _ptr(a_scale), _ptr(out), m, n, k, _stream(stream)))
+
+
 __all__ = [
     "requant_w_nvfp4_int8", "requant_a_bf16_int8", "int8_gemm_blockscaled",
     "int8_w4a8_prefill", "int8_gemm_block_partials", "quantize_bf16_nvfp4",
     "w4a4_gemm", "requant_w_blockfp8_rowwise", "quant_rowwise_fp8",
     "fp8_gemm_rowscale", "fp8_rowwise_proj", "fp8_gemv_rowscale",
-    "fp8_gemv_blockscale", "w4a16_gemv",
+    "fp8_gemv_blockscale", "w4a16_gemv", "DerivedWeights",
     "launch_count", "status_string", "abi_version", "lib", "QProjError",
 ]

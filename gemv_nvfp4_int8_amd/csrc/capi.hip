@@ -52,10 +52,11 @@ const char *qproj_status_string(int status)
     case QP_OK: return "ok";
     case QP_ERR_NULL: return "a required pointer is NULL";
     case QP_ERR_SHAPE: return "a size is zero, too large, or not a required multiple";
-    case QP_ERR_RANGE: return "GEMV row count M outside 1..16";
+    case QP_ERR_RANGE: return "GEMV row count M outside the entry point's range";
     case QP_ERR_FORMAT: return "unsupported weight format tag";
     case QP_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case QP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case QP_ERR_ALLOC: return "device memory for a derived weight could not be allocated";
     default: return "unknown status";
     }
 }

@@ -43,10 +43,11 @@ extern "C" {
 #define QP_OK 0
 #define QP_ERR_NULL (-1)   /* a required pointer is NULL                   */
 #define QP_ERR_SHAPE (-2)  /* a size is 0, too large, or breaks a multiple */
-#define QP_ERR_RANGE (-3)  /* GEMV M outside 1..16                          */
+#define QP_ERR_RANGE (-3)  /* GEMV M outside its range (1..16, or 1..8)     */
 #define QP_ERR_FORMAT (-4) /* unsupported weight format tag                 */
 #define QP_ERR_HIP (-5)    /* the HIP runtime rejected a launch             */
 #define QP_ERR_ALIGN (-6)  /* a pointer is not 16-byte aligned              */
+#define QP_ERR_ALLOC (-7)  /* a derived-weight cache could not allocate     */
 
 /* Weight format tags of an FP8 weight (dispatch_proj_rowwise.rs tests:
  * Fp8PerRow, Fp8BlockScaled, Fp8SingleScale, Bf16, Nvfp4). */
@@ -255,6 +256,65 @@ int fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
 int w4a16_gemv(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3,
                float scale2, uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                void *stream);
+
+/* ------------------------------------------------------------------------
+ * Derived-weight cache (dispatch_proj_rowwise.rs,
+ * requant_weight_rowwise_fp8_cached and its DerivedWeights cache, keyed by
+ * the weight pointer; gemm_dense_int8.rs, requant_w_nvfp4_int8 as a
+ * one-time conversion at load or lazily on first use).
+ *
+ * A cache maps (derivation, source weight address) to a requantised copy
+ * that the cache allocates with hipMalloc on the first request (a miss),
+ * fills with the stateless entry point's kernel on the caller's stream, and
+ * keeps until qproj_cache_evict or qproj_cache_destroy.  Later requests (hits)
+ * return the same device pointers, enqueue no kernel, and make the caller's
+ * stream wait for the derivation (an event recorded after it), so a derived
+ * weight may be used from any stream.  Nothing here synchronises the host.
+ * A request whose sizes (or NVFP4 scale2) differ from the entry's returns
+ * QP_ERR_SHAPE: the address then holds another weight, so evict it first.
+ * A miss is not safe under stream capture (it allocates); hits are.  All
+ * functions are thread-safe; a miss holds the cache's lock, so concurrent
+ * requests for one weight derive it once.  Errors: QP_ERR_NULL, QP_ERR_ALIGN,
+ * QP_ERR_SHAPE, QP_ERR_FORMAT as for the stateless entry points;
+ * QP_ERR_ALLOC when hipMalloc fails (nothing is inserted).
+ * ---------------------------------------------------------------------- */
+typedef struct qp_cache qp_cache;
+
+int qproj_cache_create(qp_cache **cache);
+/* Frees every derived buffer; no kernel that reads one may still be pending. */
+int qproj_cache_destroy(qp_cache *cache);
+/* Drops every derivation of the weight at `weight` (no-op if there is none);
+ * no kernel that reads one may still be pending. */
+int qproj_cache_evict(qp_cache *cache, const void *weight);
+int qproj_cache_stats(qp_cache *cache, uint64_t *entries, uint64_t *bytes);
+
+/* requant_w_blockfp8_rowwise through the cache, keyed by w.  QP_FP8_PER_ROW
+ * returns (w, scale) itself with no work, no allocation and no entry (the
+ * pages' passthrough); QP_FP8_BLOCK128 returns the cached row-wise copy
+ * (E4M3 [n,k] + F32 [n], owned by the cache). */
+int requant_w_blockfp8_rowwise_cached(qp_cache *cache, int fmt, const uint8_t *w,
+                                      const float *scale, uint32_t n, uint32_t k,
+                                      const uint8_t **w_rowwise,
+                                      const float **w_rowwise_scale, void *stream);
+/* requant_w_nvfp4_int8 through the cache, keyed by w_packed: the int8 copy
+ * [n,k] and its F32 per-32 scales [n,k/32], owned by the cache. */
+int requant_w_nvfp4_int8_cached(qp_cache *cache, const uint8_t *w_packed,
+                                const uint8_t *w_e4m3, float scale2, uint32_t n,
+                                uint32_t k, const int8_t **w_i8,
+                                const float **w_scale, void *stream);
+/* fp8_rowwise_proj with the weight requantised through the cache (the pages'
+ * cublas_fp8_rowwise_proj): no weight scratch argument. */
+int fp8_rowwise_proj_cached(qp_cache *cache, int fmt, const uint8_t *w,
+                            const float *w_scale, const uint16_t *act,
+                            uint8_t *act_q, float *act_scale, uint16_t *out,
+                            uint32_t m, uint32_t n, uint32_t k, void *stream);
+/* int8_w4a8_prefill from an NVFP4 weight, requantised to int8 through the
+ * cache on first use. */
+int int8_w4a8_prefill_cached(qp_cache *cache, const uint16_t *a_bf16,
+                             const uint8_t *w_packed, const uint8_t *w_e4m3,
+                             float scale2, int8_t *a_i8_scratch,
+                             float *a_scale_scratch, uint16_t *out, uint32_t m,
+                             uint32_t n, uint32_t k, void *stream);
 
 /* ------------------------------------------------------------------------
  * Library information.

@@ -12,6 +12,27 @@ def dev(t):
     return t.to(DEV)
 
 
+_hip = None
+
+
+def copy_from_address(ptr: int, shape, dtype) -> torch.Tensor:
+    """A device tensor holding a copy of `prod(shape)` elements at device
+    address `ptr` (memory a library cache owns), made with the HIP runtime's
+    hipMemcpy after a device synchronisation."""
+    import ctypes
+    import os
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip.hipMemcpy.restype = ctypes.c_int
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    torch.cuda.synchronize()
+    rc = _hip.hipMemcpy(t.data_ptr(), ptr, t.numel() * t.element_size(), 3)   # device to device
+    assert rc == 0, f"hipMemcpy failed ({rc})"
+    return t
+
+
 def empty(shape, dtype):
     return torch.empty(shape, dtype=dtype, device=DEV)
 

@@ -147,3 +147,63 @@ def test_block_format_checks_shape_before_any_launch():
 def test_passthrough_needs_only_the_pair():
     st, w, s = _requant(qp.QP_FP8_PER_ROW, 0xBEEF, None, None, None)
     assert st == qp.QP_ERR_NULL
+
+
+def _cache():
+    h = ctypes.c_void_p()
+    assert L.qproj_cache_create(ctypes.byref(h)) == qp.QP_OK
+    return h
+
+
+def _stats(h):
+    e, b = ctypes.c_uint64(), ctypes.c_uint64()
+    assert L.qproj_cache_stats(h, ctypes.byref(e), ctypes.byref(b)) == qp.QP_OK
+    return e.value, b.value
+
+
+def test_cache_passthrough_needs_no_work_and_no_entry():
+    """dispatch_proj_rowwise.rs, cached_requant_returns_rowwise_checkpoint_
+    pointers_without_gpu_work: a per-row weight comes back as itself, with no
+    launch and nothing allocated or cached."""
+    h = _cache()
+    try:
+        wq, sq = ctypes.c_void_p(), ctypes.c_void_p()
+        before = qp.launch_count()
+        assert L.requant_w_blockfp8_rowwise_cached(h, qp.QP_FP8_PER_ROW, FAKE, FAKE2, 128, 128,
+                                                   ctypes.byref(wq), ctypes.byref(sq), None) == qp.QP_OK
+        assert (wq.value, sq.value) == (FAKE, FAKE2)
+        assert qp.launch_count() == before
+        assert _stats(h) == (0, 0)
+    finally:
+        assert L.qproj_cache_destroy(h) == qp.QP_OK
+
+
+def test_cache_rejects_bad_calls_before_allocating():
+    h = _cache()
+    try:
+        wq, sq = ctypes.c_void_p(), ctypes.c_void_p()
+        r = lambda fmt, w, s, n, k: L.requant_w_blockfp8_rowwise_cached(
+            h, fmt, w, s, n, k, ctypes.byref(wq), ctypes.byref(sq), None)
+        before = qp.launch_count()
+        assert r(7, FAKE, FAKE2, 128, 128) == qp.QP_ERR_FORMAT
+        assert r(qp.QP_FP8_BLOCK128, FAKE, FAKE2, 200, 128) == qp.QP_ERR_SHAPE
+        assert r(qp.QP_FP8_BLOCK128, FAKE, FAKE2, 128, 0) == qp.QP_ERR_SHAPE
+        assert r(qp.QP_FP8_BLOCK128, None, FAKE2, 128, 128) == qp.QP_ERR_NULL
+        assert r(qp.QP_FP8_BLOCK128, FAKE + 8, FAKE2, 128, 128) == qp.QP_ERR_ALIGN
+        assert L.requant_w_blockfp8_rowwise_cached(h, qp.QP_FP8_BLOCK128, FAKE, FAKE2, 128, 128,
+                                                   None, ctypes.byref(sq), None) == qp.QP_ERR_NULL
+        assert L.requant_w_nvfp4_int8_cached(h, FAKE, FAKE2, 1.0, 64, 48, ctypes.byref(wq),
+                                             ctypes.byref(sq), None) == qp.QP_ERR_SHAPE
+        # the projections check their own arguments before deriving anything
+        assert L.fp8_rowwise_proj_cached(h, qp.QP_FP8_BLOCK128, FAKE, FAKE2, None, FAKE, FAKE,
+                                         FAKE, 4, 128, 128, None) == qp.QP_ERR_NULL
+        assert L.int8_w4a8_prefill_cached(h, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, 4, 64, 48,
+                                          None) == qp.QP_ERR_SHAPE
+        assert L.qproj_cache_evict(h, FAKE) == qp.QP_OK          # nothing to evict
+        assert qp.launch_count() == before
+        assert _stats(h) == (0, 0)
+    finally:
+        assert L.qproj_cache_destroy(h) == qp.QP_OK
+    assert L.qproj_cache_create(None) == qp.QP_ERR_NULL
+    assert L.qproj_cache_destroy(None) == qp.QP_ERR_NULL
+    assert qp.status_string(qp.QP_ERR_ALLOC) != "unknown status"

@@ -12,8 +12,8 @@ import torch
 import gemv_nvfp4_int8_amd as qp
 import oracle
 import synth
-from tests.gpu_util import (assert_gemm_close, assert_gemv_close, bits, dev,
-                            empty, filled, host)
+from tests.gpu_util import (assert_gemm_close, assert_gemv_close, bits,
+                            copy_from_address, dev, empty, filled, host)
 
 pytestmark = pytest.mark.gpu
 
@@ -391,3 +391,102 @@ def test_w4a16_gemv_batched_rows_bit_identical_to_single_row(n, k):
         o = empty((m, n), torch.bfloat16)
         qp.w4a16_gemv(x[:m], wpd, wsd, s2, o)
         assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
+
+
+# ---------------------------------------------------------------------------
+# Derived-weight cache (dispatch_proj_rowwise.rs, requant_weight_rowwise_fp8_
+# cached and DerivedWeights; gemm_dense_int8.rs, lazy first-use requant).
+def test_cache_derives_once_and_matches_the_oracle():
+    m, n, k = 64, 256, 384
+    cse = synth.fp8_block("cpu", m, n, k)
+    w, g = dev(cse.w_block), dev(cse.block_grid)
+    c = qp.DerivedWeights()
+    try:
+        before = qp.launch_count()
+        p1 = c.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w, g)
+        assert qp.launch_count() == before + 1
+        assert c.stats() == (1, n * k + 4 * n)
+        p2 = c.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w, g)
+        assert p2 == p1 and qp.launch_count() == before + 1          # a hit: no launch
+        ow, ows = oracle.requant_w_blockfp8_rowwise(bits(cse.w_block), cse.block_grid.numpy())
+        wq = copy_from_address(p1[0], (n, k), torch.uint8)
+        ws = copy_from_address(p1[1], (n,), torch.float32)
+        assert np.array_equal(host(wq), ow) and np.array_equal(host(ws), ows)
+        # the same address asked for with other sizes holds another weight
+        with pytest.raises(qp.QProjError) as err:
+            c.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w[:128], g[:1])
+        assert err.value.status == qp.QP_ERR_SHAPE
+        # a second weight is a second entry; eviction drops only the first
+        w2 = w.clone()
+        c.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w2, g)
+        assert c.stats() == (2, 2 * (n * k + 4 * n))
+        c.evict(w)
+        assert c.stats() == (1, n * k + 4 * n)
+        before = qp.launch_count()
+        c.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w, g)
+        assert qp.launch_count() == before + 1                        # derived again
+        # a per-row weight passes through untouched
+        assert c.requant_w_blockfp8_rowwise(qp.QP_FP8_PER_ROW, wq, ws) == (wq.data_ptr(), ws.data_ptr())
+        assert c.stats() == (2, 2 * (n * k + 4 * n))
+    finally:
+        c.close()
+
+
+def test_cached_projection_equals_stateless_across_streams():
+    """Derive on a side stream, then use the hit on the current stream
+    without synchronising the side stream: the hit orders the projection
+    after the derivation."""
+    m, n, k = 130, 384, 640
+    cse = synth.fp8_block("cpu", m, n, k)
+    w, g, a = dev(cse.w_block), dev(cse.block_grid), dev(cse.a_bf16)
+    aq, asc = empty((m, k), torch.uint8), empty((m,), torch.float32)
+    ref = filled((m, n), torch.bfloat16)
+    wr, wrs = empty((n, k), torch.uint8), empty((n,), torch.float32)
+    qp.fp8_rowwise_proj(qp.QP_FP8_BLOCK128, w, g, wr, wrs, a, aq, asc, ref)
+    c = qp.DerivedWeights()
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        c.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w, g, stream=side)
+        out = filled((m, n), torch.bfloat16)
+        aq2, asc2 = empty((m, k), torch.uint8), empty((m,), torch.float32)
+        c.fp8_rowwise_proj(qp.QP_FP8_BLOCK128, w, g, a, aq2, asc2, out)
+        assert torch.equal(host_t(out), host_t(ref))
+        assert c.stats()[0] == 1
+    finally:
+        torch.cuda.synchronize()
+        c.close()
+
+
+def test_cached_int8_prefill_equals_stateless():
+    m, n, k = 96, 320, 512
+    cse = synth.w4a8_prefill("cpu", m, n, k)
+    wb, a = dev(cse.w_bf16), dev(cse.a_bf16)
+    wp, we = empty((n, k // 2), torch.uint8), empty((n, k // 16), torch.uint8)
+    qp.quantize_bf16_nvfp4(wb, wp, we, cse.scale2)
+    wi8, wsc = empty((n, k), torch.int8), empty((n, k // 32), torch.float32)
+    qp.requant_w_nvfp4_int8(wp, we, cse.scale2, wi8, wsc)
+    ai8, asc = empty((m, k), torch.int8), empty((m, k // 32), torch.float32)
+    ref = filled((m, n), torch.bfloat16)
+    qp.int8_w4a8_prefill(a, wi8, wsc, ai8, asc, ref)
+    c = qp.DerivedWeights()
+    try:
+        out = filled((m, n), torch.bfloat16)
+        c.int8_w4a8_prefill(a, wp, we, cse.scale2, ai8, asc, out)
+        before = qp.launch_count()
+        c.int8_w4a8_prefill(a, wp, we, cse.scale2, ai8, asc, out)
+        assert qp.launch_count() == before + 2                        # act requant + GEMM only
+        assert torch.equal(host_t(out), host_t(ref))
+        p = c.requant_w_nvfp4_int8(wp, we, cse.scale2)
+        assert torch.equal(host_t(copy_from_address(p[0], (n, k), torch.int8)), host_t(wi8))
+        assert torch.equal(host_t(copy_from_address(p[1], (n, k // 32), torch.float32)), host_t(wsc))
+        with pytest.raises(qp.QProjError) as err:                     # another scale2: another weight
+            c.requant_w_nvfp4_int8(wp, we, cse.scale2 * 2)
+        assert err.value.status == qp.QP_ERR_SHAPE
+    finally:
+        c.close()
+
+
+def host_t(t):
+    torch.cuda.synchronize()
+    return t.cpu().view(torch.uint8) if t.dtype != torch.uint8 else t.cpu()
