@@ -20,7 +20,9 @@ The same line carries:
                 GEMMs in TFLOP/s against the MFMA peak of their data type,
                 the block-scaled FP8 GEMV (128 x 128 F32 block scales)
                 at the decode shapes for M in {1, 2, 4}, and the NVFP4-weight
-                GEMV (W4A16) there for M in {1, 2, 8}, in GB/s.
+                GEMV (W4A16) there for M in {1, 2, 8}, in GB/s;
+  ablations     the W4A4 GEMM under three workgroup -> tile orders, and a
+                tile GEMM against the GEMV at M = 8 on the lm_head weight.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
 """
@@ -52,8 +54,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="GEMV step only")
     ap.add_argument("--only", default="", help="comma list of secondary items to run")
@@ -91,11 +93,19 @@ def gemv_bytes(m, n, k):
     return n * k + 4 * n + 2 * m * k + 2 * m * n
 
 
-def time_launches(fn, iters, warm=2):
+def time_launches(fn, iters, warm=2, warm_ms=30.0):
     """Average duration (ms) of `fn` launched back to back on the current
-    stream, measured with HIP events recorded on that stream."""
+    stream, measured with HIP events recorded on that stream.  Untimed
+    launches run first for at least `warm_ms` (the shader clock ramps up over
+    the first tens of milliseconds of load) and at least `warm` times."""
     import torch
-    for i in range(warm):
+    fn(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn(1)
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t0, 1e-6)
+    for i in range(max(warm, int(warm_ms * 1e-3 / est))):
         fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -418,6 +428,62 @@ def run_secondary(qp, synth, dev, only):
         gemm_item("w4a4_gemm", 2 * m * n * k,
                   lambda: qp.w4a4_gemm(ap_, as_, wp, ws, out, 1.0, c.scale_w2), "fp16")
         del c, a_src, ap_, as_, wp, ws, out
+        torch.cuda.empty_cache()
+
+    # Ablations (gemm_fp4.rs: w4a4_gemm's N-fast grid against
+    # w4a4_gemm_mfast's M-fast grid; fp8_gemv_batch.rs: tile GEMMs that pad
+    # M to their tile against the batched GEMV at M = 8).
+    if want("ablations"):
+        m, n, k = 4096, 5120, 17408
+        c = synth.w4a4_prefill(dev, m, n, k)
+        ap_ = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+        wp = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        ws = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        qp.quantize_bf16_nvfp4(c.a_bf16, ap_, as_, 1.0)
+        qp.quantize_bf16_nvfp4(c.w_bf16, wp, ws, c.scale_w2)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        orders = {}
+        for name, order in (("banded_xcd", qp.QP_TILES_BANDED), ("m_fast", qp.QP_TILES_MFAST),
+                            ("n_fast", qp.QP_TILES_NFAST)):
+            ms = time_launches(lambda i: qp.w4a4_gemm(ap_, as_, wp, ws, out, 1.0, c.scale_w2,
+                                                      tile_order=order), iters=10)
+            tf = 2 * m * n * k / (ms * 1e-3) / 1e12
+            orders[name] = {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
+                            "frac_fp16": round(tf / PEAK_TFLOPS["fp16"], 4)}
+            log(f"  ablation w4a4 tiles {name}: {ms*1e3:.1f} us  {tf:.1f} TFLOP/s")
+        res["ablation_w4a4_tile_order"] = {"shape": [m, n, k], "orders": orders}
+        del c, ap_, as_, wp, ws, out
+        torch.cuda.empty_cache()
+
+        m, n, k = 8, 152064, 5120
+        wb = synth.gemv_weight_bf16(n, k, dev, shape_id=2)
+        wq = torch.empty((n, k), dtype=torch.uint8, device=dev)
+        wsr = torch.empty((n,), dtype=torch.float32, device=dev)
+        qp.quant_rowwise_fp8(wb, wq, wsr)
+        del wb
+        copies = [(wq, wsr), (wq.clone(), wsr.clone())]
+        x = synth.gemv_acts_bf16(m, k, dev, shape_id=2)
+        aq = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        asr = torch.empty((m,), dtype=torch.float32, device=dev)
+        qp.quant_rowwise_fp8(x, aq, asr)
+        o = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ms_gemm = time_launches(lambda i: qp.fp8_gemm_rowscale(
+            aq, asr, copies[i % 2][0], copies[i % 2][1], o), iters=20)
+        ms_gemv = time_launches(lambda i: qp.fp8_gemv_rowscale(
+            x, copies[i % 2][0], copies[i % 2][1], o), iters=20)
+        wbytes = n * k + 4 * n
+        res["ablation_m8_tile_gemm_vs_gemv"] = {
+            "shape": [m, n, k],
+            "tile_gemm": {"kernel": "fp8_gemm_rowscale (128x128 tiles, M padded to 128)",
+                          "us": round(ms_gemm * 1e3, 1),
+                          "weight_GBs": round(wbytes / (ms_gemm * 1e-3) / 1e9, 1)},
+            "gemv": {"kernel": "fp8_gemv_rowscale", "us": round(ms_gemv * 1e3, 1),
+                     "weight_GBs": round(wbytes / (ms_gemv * 1e-3) / 1e9, 1)}}
+        log(f"  ablation M=8 lm_head: tile GEMM {ms_gemm*1e3:.1f} us "
+            f"({wbytes / (ms_gemm * 1e-3) / 1e9:.0f} GB/s) vs GEMV {ms_gemv*1e3:.1f} us "
+            f"({wbytes / (ms_gemv * 1e-3) / 1e9:.0f} GB/s)")
+        del copies, wq, wsr, x, aq, asr, o
         torch.cuda.empty_cache()
 
     # Block FP8 -> row-wise FP8 requant + row-wise FP8 GEMM, M = 8192.

@@ -36,6 +36,10 @@ QP_FP8_SINGLE_SCALE = 2
 QP_BF16 = 3
 QP_NVFP4 = 4
 
+QP_TILES_BANDED = 0
+QP_TILES_MFAST = 1
+QP_TILES_NFAST = 2
+
 
 class QProjError(RuntimeError):
     def __init__(self, fn: str, status: int):
@@ -66,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "int8_gemm_block_partials": [P, P, P, U, U, U, P],
             "quantize_bf16_nvfp4": [P, P, P, F, U, U, P],
             "w4a4_gemm": [P, P, P, P, P, F, F, U, U, U, P],
+            "w4a4_gemm_tiles": [P, P, P, P, P, F, F, U, U, U, I, P],
             "requant_w_blockfp8_rowwise": [I, P, P, P, P, PP, PP, U, U, P],
             "quant_rowwise_fp8": [P, P, P, U, U, P],
             "fp8_gemm_rowscale": [P, P, P, P, P, U, U, U, P],
@@ -218,7 +223,8 @@ def quantize_bf16_nvfp4(x, packed, scale, scale2=1.0, stream=None):
 
 
 def w4a4_gemm(a_packed, a_scale, w_packed, w_scale, out, scale_a2, scale_w2,
-              stream=None):
+              stream=None, tile_order=None):
+    """tile_order: None (w4a4_gemm) or one of QP_TILES_* (w4a4_gemm_tiles)."""
     m, kh = a_packed.shape
     n = w_packed.shape[0]
     k = 2 * kh
@@ -227,9 +233,14 @@ def w4a4_gemm(a_packed, a_scale, w_packed, w_scale, out, scale_a2, scale_w2,
     _need(w_packed, "w_packed", U8, (n, kh))
     _need(w_scale, "w_scale", U8, (n, k // 16))
     _need(out, "out", BF16, (m, n))
-    _check("w4a4_gemm", lib().w4a4_gemm(
-        _ptr(a_packed), _ptr(a_scale), _ptr(w_packed), _ptr(w_scale), _ptr(out),
-        float(scale_a2), float(scale_w2), m, n, k, _stream(stream)))
+    if tile_order is None:
+        _check("w4a4_gemm", lib().w4a4_gemm(
+            _ptr(a_packed), _ptr(a_scale), _ptr(w_packed), _ptr(w_scale), _ptr(out),
+            float(scale_a2), float(scale_w2), m, n, k, _stream(stream)))
+    else:
+        _check("w4a4_gemm_tiles", lib().w4a4_gemm_tiles(
+            _ptr(a_packed), _ptr(a_scale), _ptr(w_packed), _ptr(w_scale), _ptr(out),
+            float(scale_a2), float(scale_w2), m, n, k, int(tile_order), _stream(stream)))
 
 
 def requant_w_blockfp8_rowwise(fmt, w, scale, w_out=None, scale_out=None,

@@ -145,6 +145,18 @@ int w4a4_gemm(const uint8_t *a_packed, const uint8_t *a_scale,
               float scale_a2, float scale_w2, uint32_t m, uint32_t n,
               uint32_t k, void *stream)
 {
+    return w4a4_gemm_tiles(a_packed, a_scale, w_packed, w_scale, out, scale_a2, scale_w2,
+                           m, n, k, QP_TILES_BANDED, stream);
+}
+
+int w4a4_gemm_tiles(const uint8_t *a_packed, const uint8_t *a_scale,
+                    const uint8_t *w_packed, const uint8_t *w_scale, uint16_t *out,
+                    float scale_a2, float scale_w2, uint32_t m, uint32_t n,
+                    uint32_t k, int tile_order, void *stream)
+{
+    if (tile_order != QP_TILES_BANDED && tile_order != QP_TILES_MFAST &&
+        tile_order != QP_TILES_NFAST)
+        return QP_ERR_FORMAT;
     if (!a_packed || !a_scale || !w_packed || !w_scale || !out)
         return QP_ERR_NULL;
     if (!aligned16(a_packed) || !aligned16(w_packed) || !aligned16(out))
@@ -153,7 +165,8 @@ int w4a4_gemm(const uint8_t *a_packed, const uint8_t *a_scale,
         !fits(n, k) || !fits(m, n))
         return QP_ERR_SHAPE;
     return done(qp::launch_w4a4_gemm(a_packed, a_scale, w_packed, w_scale, out,
-                                     scale_a2, scale_w2, m, n, k, S(stream)));
+                                     scale_a2, scale_w2, m, n, k, (uint32_t)tile_order,
+                                     S(stream)));
 }
 
 int requant_w_blockfp8_rowwise(int fmt, const uint8_t *w, const float *scale,

@@ -49,6 +49,24 @@ __device__ __forceinline__ void tile_coords(uint32_t mtiles, uint32_t ntiles,
     tile_coords_of(blockIdx.x, mtiles, ntiles, tm, tn);
 }
 
+// Tile orders a launch may ask for (the tile-order ablation): 0 = the banded,
+// XCD-aware order above; 1 = plain M-fast (workgroup id = tm + mtiles * tn,
+// consecutive workgroups share a weight panel); 2 = plain N-fast (consecutive
+// workgroups share an activation panel).
+__device__ __forceinline__ void tile_coords_order(uint32_t order, uint32_t mtiles,
+                                                  uint32_t ntiles, uint32_t &tm, uint32_t &tn)
+{
+    if (order == 1) {
+        tm = blockIdx.x % mtiles;
+        tn = blockIdx.x / mtiles;
+    } else if (order == 2) {
+        tn = blockIdx.x % ntiles;
+        tm = blockIdx.x / ntiles;
+    } else {
+        tile_coords(mtiles, ntiles, tm, tn);
+    }
+}
+
 // Cooperative predicated copy of a ROWS x BKB-byte operand stage from global
 // memory (row stride ld bytes) into registers: 16-byte chunks, chunk c of
 // thread t is c = t + 256*j.  Rows >= nrows or columns >= kbytes load zero.

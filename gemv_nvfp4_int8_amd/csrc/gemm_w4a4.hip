@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_w4a4_gemm(
     const uint8_t *__restrict__ Ap, const uint8_t *__restrict__ Asc,
     const uint8_t *__restrict__ Wp, const uint8_t *__restrict__ Wsc,
     uint16_t *__restrict__ out, float s2, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t mtiles, uint32_t ntiles)
+    uint32_t mtiles, uint32_t ntiles, uint32_t order)
 {
     __shared__ __attribute__((aligned(16))) uint8_t sA[2][W4_BM * W4_PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t sW[2][W4_BN * W4_PITCH];
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_w4a4_gemm(
     __shared__ __attribute__((aligned(16))) uint8_t sWs[2][W4_BN * W4_NSC];
 
     uint32_t tm, tn;
-    tile_coords(mtiles, ntiles, tm, tn);
+    tile_coords_order(order, mtiles, ntiles, tm, tn);
     const uint32_t m0 = tm * W4_BM, n0 = tn * W4_BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     const uint8_t *__restrict__ Ap, const uint8_t *__restrict__ Asc,
     const uint8_t *__restrict__ Wp, const uint8_t *__restrict__ Wsc,
     uint16_t *__restrict__ out, float s2, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t mtiles, uint32_t ntiles)
+    uint32_t mtiles, uint32_t ntiles, uint32_t order)
 {
     constexpr int NW = 2 * WM;            // waves
     constexpr int RW = WB_TM / WM;        // rows per wave
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     __shared__ __attribute__((aligned(1024))) uint8_t B1[WB_BUF];
 
     uint32_t tm, tn;
-    tile_coords(mtiles, ntiles, tm, tn);
+    tile_coords_order(order, mtiles, ntiles, tm, tn);
     const uint32_t m0 = tm * WB_TM, n0 = tn * WB_TN;
     const uint32_t m0e = min(m0, M - WB_TM), n0e = min(n0, N - WB_TN);
     const int lane = threadIdx.x & 63;
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
 hipError_t launch_w4a4_gemm(const uint8_t *ap, const uint8_t *asc,
                             const uint8_t *wp, const uint8_t *wsc, uint16_t *out,
                             float sa2, float sw2, uint32_t m, uint32_t n,
-                            uint32_t k, hipStream_t st)
+                            uint32_t k, uint32_t order, hipStream_t st)
 {
     float s2 = sa2 * sw2;
     if (k % WB_KE == 0 && m >= (uint32_t)WB_TM && n >= (uint32_t)WB_TN) {
@@ -420,11 +420,11 @@ hipError_t launch_w4a4_gemm(const uint8_t *ap, const uint8_t *asc,
         // WM = 2 (four waves, 128 x 80 each): two waves per SIMD (WM = 4)
         // measured slower at 4096 x 5120 x 17408 (778 vs 736 us)
         hipLaunchKernelGGL(k_w4a4_gemm_big<2>, dim3(mt * nt), dim3(256), 0, st,
-                           ap, asc, wp, wsc, out, s2, m, n, k, mt, nt);
+                           ap, asc, wp, wsc, out, s2, m, n, k, mt, nt, order);
     } else {
         uint32_t mt = (m + W4_BM - 1) / W4_BM, nt = (n + W4_BN - 1) / W4_BN;
         hipLaunchKernelGGL(k_w4a4_gemm, dim3(mt * nt), dim3(256), 0, st,
-                           ap, asc, wp, wsc, out, s2, m, n, k, mt, nt);
+                           ap, asc, wp, wsc, out, s2, m, n, k, mt, nt, order);
     }
     count_launch();
     return hipGetLastError();

@@ -37,10 +37,12 @@ hipError_t launch_fp8_gemm_rowscale(const uint8_t *a, const float *as,
                                     const uint8_t *w, const float *ws,
                                     uint16_t *out, uint32_t m, uint32_t n,
                                     uint32_t k, hipStream_t st);
+// order: the workgroup -> tile mapping (0 banded XCD-aware, 1 M-fast,
+// 2 N-fast; see tile_coords_order).
 hipError_t launch_w4a4_gemm(const uint8_t *ap, const uint8_t *asc,
                             const uint8_t *wp, const uint8_t *wsc, uint16_t *out,
                             float sa2, float sw2, uint32_t m, uint32_t n,
-                            uint32_t k, hipStream_t st);
+                            uint32_t k, uint32_t order, hipStream_t st);
 
 // Counts kernel launches enqueued by the library (all launchers add to it).
 void count_launch(uint32_t n = 1);

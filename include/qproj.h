@@ -146,6 +146,24 @@ int w4a4_gemm(const uint8_t *a_packed, const uint8_t *a_scale,
               float scale_a2, float scale_w2, uint32_t m, uint32_t n,
               uint32_t k, void *stream);
 
+/* w4a4_gemm with a chosen workgroup -> output-tile order, for the tile-order
+ * ablation of gemm_fp4.rs (w4a4_gemm with an N-fast grid against
+ * w4a4_gemm_mfast, whose M-fast grid lets neighbouring workgroups reuse one
+ * weight panel):
+ *   QP_TILES_BANDED  bands of 8 M-tiles walked M-fast, each XCD given a
+ *                    contiguous range of workgroups (what w4a4_gemm uses);
+ *   QP_TILES_MFAST   workgroup id = m-tile + (m-tiles) * n-tile;
+ *   QP_TILES_NFAST   workgroup id = n-tile + (n-tiles) * m-tile.
+ * Every order computes each output element identically (same bits).
+ * Any other value: QP_ERR_FORMAT. */
+#define QP_TILES_BANDED 0
+#define QP_TILES_MFAST 1
+#define QP_TILES_NFAST 2
+int w4a4_gemm_tiles(const uint8_t *a_packed, const uint8_t *a_scale,
+                    const uint8_t *w_packed, const uint8_t *w_scale, uint16_t *out,
+                    float scale_a2, float scale_w2, uint32_t m, uint32_t n,
+                    uint32_t k, int tile_order, void *stream);
+
 /* ------------------------------------------------------------------------
  * Block-scaled FP8 -> row-wise FP8 weight requant
  * (dispatch_proj_rowwise.rs, rowwise_pair_passthrough and

@@ -207,3 +207,11 @@ def test_cache_rejects_bad_calls_before_allocating():
     assert L.qproj_cache_create(None) == qp.QP_ERR_NULL
     assert L.qproj_cache_destroy(None) == qp.QP_ERR_NULL
     assert qp.status_string(qp.QP_ERR_ALLOC) != "unknown status"
+
+
+def test_w4a4_tile_order_must_be_known():
+    for order in (-1, 3, 99):
+        assert L.w4a4_gemm_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 64, 64, 64, order,
+                                 None) == qp.QP_ERR_FORMAT
+    assert L.w4a4_gemm_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 64, 64, 48,
+                             qp.QP_TILES_NFAST, None) == qp.QP_ERR_SHAPE

@@ -490,3 +490,23 @@ def test_cached_int8_prefill_equals_stateless():
 def host_t(t):
     torch.cuda.synchronize()
     return t.cpu().view(torch.uint8) if t.dtype != torch.uint8 else t.cpu()
+
+
+@pytest.mark.parametrize("m,n,k", [(520, 500, 1280), (200, 300, 96)])
+def test_w4a4_tile_orders_agree_bit_for_bit(m, n, k):
+    """The tile-order ablation (gemm_fp4.rs, w4a4_gemm against
+    w4a4_gemm_mfast) changes only which workgroup computes which tile."""
+    a = _bf16_rows((m, k), 71)
+    w = _bf16_rows((n, k), 72, std=0.02)
+    ap, asc = empty((m, k // 2), torch.uint8), empty((m, k // 16), torch.uint8)
+    wp, wsc = empty((n, k // 2), torch.uint8), empty((n, k // 16), torch.uint8)
+    qp.quantize_bf16_nvfp4(dev(a), ap, asc, 1.0)
+    qp.quantize_bf16_nvfp4(dev(w), wp, wsc, 0.01)
+    outs = []
+    for order in (qp.QP_TILES_BANDED, qp.QP_TILES_MFAST, qp.QP_TILES_NFAST):
+        o = filled((m, n), torch.bfloat16)
+        qp.w4a4_gemm(ap, asc, wp, wsc, o, 1.0, 0.01, tile_order=order)
+        outs.append(host(o))
+    ref = oracle.w4a4_gemm(host(ap), host(asc), host(wp), host(wsc), 1.0, 0.01)
+    assert_gemm_close(outs[0], ref, "w4a4 banded")
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
