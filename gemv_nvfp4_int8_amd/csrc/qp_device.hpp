@@ -122,16 +122,18 @@ struct ScaleDiv {
         fast = s_ >= 0x1p-100f && s_ <= 0x1p100f;
         r = fast ? div_rn(1.0f, s_) : 0.0f;
     }
+    // The FMA-corrected quotient alone (valid when `fast`), without a branch.
+    __device__ __forceinline__ float quick(float x) const
+    {
+        float q0 = x * r;
+        float rem = __builtin_fmaf(-q0, s, x);
+        float q = __builtin_fmaf(rem, r, q0);
+        return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) |
+                               (__float_as_uint(q0) & 0x80000000u));
+    }
     __device__ __forceinline__ float operator()(float x) const
     {
-        if (fast) {
-            float q0 = x * r;
-            float rem = __builtin_fmaf(-q0, s, x);
-            float q = __builtin_fmaf(rem, r, q0);
-            return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) |
-                                   (__float_as_uint(q0) & 0x80000000u));
-        }
-        return div_rn(x, s);
+        return fast ? quick(x) : div_rn(x, s);
     }
 };
 

@@ -4,6 +4,8 @@
 // loads, codes are written with 8- or 16-byte stores, and absmax reductions
 // stay in registers (per-block kernels) or use wave shuffles plus one LDS
 // exchange per workgroup (per-row kernels).
+#include <type_traits>
+
 #include "qp_device.hpp"
 #include "qp_launch.hpp"
 
@@ -258,6 +260,18 @@ __device__ __forceinline__ float block_max_256(float v, float *red)
 
 // E4M3 codes of v[0..7] / sc (correctly rounded quotients) in two dwords;
 // all +0 when the scale is 0.
+// E4M3 codes of v[0..7] / d.s for a scale whose `fast` flag is known to be
+// FAST (callers branch once per scale, not once per element).
+template <bool FAST>
+__device__ __forceinline__ u32x2 enc8_e4m3_path(const float *v, const ScaleDiv &d)
+{
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        t[i] = FAST ? d.quick(v[i]) : div_rn(v[i], d.s);
+    return (u32x2){cvt_e4m3x4(t[0], t[1], t[2], t[3]), cvt_e4m3x4(t[4], t[5], t[6], t[7])};
+}
+
 __device__ __forceinline__ u32x2 enc8_e4m3(const float *v, const ScaleDiv &d, bool zero)
 {
     u32x2 o = {0, 0};
@@ -516,20 +530,33 @@ __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_wave(
     amax = wave_max(amax);
     const float sc = div_rn(amax, 448.0f);
     const ScaleDiv dv(sc);
+    // The scale is one per row (wave-uniform): pick the division path once.
+    auto encode = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const uint32_t c = lane + 64u * j;
-        if (c < nch) {
-            float v[16];
+        for (int j = 0; j < CPL; ++j) {
+            const uint32_t c = lane + 64u * j;
+            if (c < nch) {
+                float v[16];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                v[2 * i] = bf16_lo(yb[j][i]);
-                v[2 * i + 1] = bf16_hi(yb[j][i]);
+                for (int i = 0; i < 8; ++i) {
+                    v[2 * i] = bf16_lo(yb[j][i]);
+                    v[2 * i + 1] = bf16_hi(yb[j][i]);
+                }
+                u32x4 o = {0, 0, 0, 0};
+                if (sc != 0.0f) {
+                    const u32x2 lo = enc8_e4m3_path<FAST>(&v[0], dv);
+                    const u32x2 hi = enc8_e4m3_path<FAST>(&v[8], dv);
+                    o = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+                }
+                *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = o;
             }
-            const u32x2 lo = enc8_e4m3(&v[0], dv, sc == 0.0f), hi = enc8_e4m3(&v[8], dv, sc == 0.0f);
-            *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
         }
-    }
+    };
+    if (dv.fast)
+        encode(std::true_type{});
+    else
+        encode(std::false_type{});
     if (lane == 0)
         s[row] = sc;
 }

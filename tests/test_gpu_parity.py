@@ -90,8 +90,12 @@ def test_quant_rowwise_fp8_bit_exact(rows, k):
     assert np.array_equal(host(q), oq)
 
 
-@pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 5120)])
+@pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 5120), (1152, 1024),
+                                 (640, 8192), (256, 2176)])
 def test_requant_blockfp8_rowwise_bit_exact(n, k):
+    # k / 16 / 64 chunks per lane: 1 (partly and wholly used), 5, 8, and 3
+    # with the third partly used; the row-pipelined kernel takes several rows
+    # per wave once n exceeds its resident waves.
     cse = synth.fp8_block("cpu", m=1, n=n, k=k)
     w, grid = cse.w_block.clone(), cse.block_grid
     w[1, ::5] = 0x80                     # -0.0 codes
