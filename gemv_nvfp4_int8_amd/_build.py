@@ -10,9 +10,10 @@ the source tree.  Flags:
                                          code rounding relies on
   -target-feature -packed-fp32-ops       no packed-FP32 VALU instructions
 Per file (FILE_FLAGS):
-  gemv_w4a16.hip: -mllvm -amdgpu-mfma-vgpr-form   MFMA results in ordinary
-                                         VGPRs: its kernels fold every MFMA
-                                         result with VALU FMAs, and the
+  gemv_w4a16.hip, gemm_int8.hip: -mllvm -amdgpu-mfma-vgpr-form
+                                         MFMA results in ordinary VGPRs:
+                                         these kernels fold every MFMA result
+                                         with VALU FMAs, and the
                                          accumulator-register form costs a
                                          copy per value read
 """
@@ -42,6 +43,7 @@ DEVICE_FLAGS = [
 
 FILE_FLAGS = {
     "gemv_w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_int8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
