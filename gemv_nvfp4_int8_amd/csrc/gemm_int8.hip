@@ -10,6 +10,14 @@
 // accumulator.  The block scales of a stage are staged in LDS next to the
 // operand tiles.  The same tile code can instead write every P_b to memory
 // (the block-partials test export).
+//
+// The fold is the kernel's bound: with no packed FP32 math it costs the
+// vector ALU 4 cycles per wave instruction, against 32 cycles for the int8
+// MFMA of a whole 32x32x32 block.  It therefore keeps the VALU work per
+// output and block at two instructions (the scale product moves to the
+// matrix core) and feeds the VALU without stalls: operand stages arrive by
+// LDS-DMA, which holds no registers, so the next tile's MFMAs can be in
+// flight while the current tile is folded.
 #include "gemm_common.hpp"
 #include "qp_launch.hpp"
 
@@ -17,7 +25,33 @@ namespace qp {
 
 constexpr int I8_BM = 128, I8_BN = 128, I8_BK = 128;   // BK in bytes = elements
 constexpr int I8_KB = I8_BK / 32;                       // K blocks per stage
-constexpr int I8_PITCH = I8_BK + 16;
+constexpr int I8_SLOT = I8_BM * I8_BK;                  // one operand stage, 16 KB
+
+// DMA one operand stage: rows row0 .. row0+127 (clamped to nrows-1), bytes
+// k0 .. k0+127 of each row, into a 16 KB slot.  Rows are 128 bytes,
+// unpadded, with the 16-byte chunks XOR-swizzled as in swz(): instruction j
+// of wave w fills kilobyte 4w+j = rows 8(4w+j) .. +7, lane i landing in row
+// i/8, physical chunk i%8, which holds logical chunk (i%8) ^ swz.  A chunk
+// past the end of K (only in the last stage when K % 128 != 0) is loaded
+// from the row's first chunk instead: its K block has zero scales, so it
+// adds exactly zero, and the load stays in bounds.
+__device__ __forceinline__ void i8_dma_stage(const int8_t *__restrict__ base, uint32_t K,
+                                             uint32_t row0, uint32_t nrows, uint32_t k0,
+                                             uint8_t *slot)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kbyte = 4 * wave + j;
+        const int row = 8 * kbyte + (lane >> 3);
+        uint32_t gr = row0 + row;
+        gr = gr < nrows ? gr : nrows - 1;
+        uint32_t gk = k0 + 16u * (uint32_t)swz(row, lane & 7);
+        gk = gk < K ? gk : 0u;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(base) + (size_t)gr * K + gk,
+                                         (lds_void *)(slot + 1024 * kbyte), 16, 0, 0);
+    }
+}
 
 template <bool PARTIALS>
 __global__ __launch_bounds__(256) void k_int8_gemm(
@@ -26,11 +60,15 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
     uint16_t *__restrict__ out, int32_t *__restrict__ part,
     uint32_t M, uint32_t N, uint32_t K, uint32_t mtiles, uint32_t ntiles)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2][I8_BM * I8_PITCH];
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][I8_BN * I8_PITCH];
-    // scales stored block-major so 4 consecutive rows are one 16-byte read
-    __shared__ __attribute__((aligned(16))) float sAs[2][I8_KB][I8_BM];
-    __shared__ __attribute__((aligned(16))) float sWs[2][I8_KB][I8_BN];
+    // Four separately named slots: every access below names its slot
+    // statically, so the compiler sees that the DMA into the next stage's
+    // slots cannot alias the reads of the current ones and does not wait
+    // for it.
+    __shared__ __attribute__((aligned(1024))) uint8_t sA0[I8_SLOT], sA1[I8_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW0[I8_SLOT], sW1[I8_SLOT];
+    // scales stored row-major: a row's four K blocks are one 16-byte read
+    __shared__ __attribute__((aligned(16))) float sAs[2][I8_BM][I8_KB];
+    __shared__ __attribute__((aligned(16))) float sWs[2][I8_BN][I8_KB];
 
     uint32_t tm, tn;
     tile_coords(mtiles, ntiles, tm, tn);
@@ -38,15 +76,12 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t nb = K / 32;
+    const uint32_t nst = (K + I8_BK - 1) / I8_BK;
 
-    StageLoader<I8_BM, I8_BK> la;
-    StageLoader<I8_BN, I8_BK> lw;
     float ras[2], rws[2];   // 512 scale values per operand per stage / 256 threads
-
-    auto load_stage = [&](uint32_t kst) {
-        uint32_t k0 = kst * I8_BK;
-        la.load(reinterpret_cast<const uint8_t *>(A), K, m0, M, k0, K);
-        lw.load(reinterpret_cast<const uint8_t *>(W), K, n0, N, k0, K);
+    auto load_stage = [&](uint32_t kst, uint8_t *la, uint8_t *lw) {
+        i8_dma_stage(A, K, m0, M, kst * I8_BK, la);
+        i8_dma_stage(W, K, n0, N, kst * I8_BK, lw);
         if constexpr (!PARTIALS) {      // the partials export has no scales
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -58,18 +93,20 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
             }
         }
     };
-    auto store_stage = [&](int buf) {
-        la.store(sA[buf]);
-        lw.store(sW[buf]);
+    auto store_scales = [&](int buf) {
         if constexpr (!PARTIALS) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 int c = threadIdx.x + 256 * j;
-                int row = c / I8_KB, b = c % I8_KB;
-                sAs[buf][b][row] = ras[j];
-                sWs[buf][b][row] = rws[j];
+                sAs[buf][c / I8_KB][c % I8_KB] = ras[j];
+                sWs[buf][c / I8_KB][c % I8_KB] = rws[j];
             }
         }
+    };
+    // wait for this wave's DMA and LDS accesses, then for every wave's
+    auto sync_stage = [&]() {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        __syncthreads();
     };
 
     f32x16 acc[2][2];
@@ -81,75 +118,104 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    const uint32_t nst = (K + I8_BK - 1) / I8_BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
+    load_stage(0, sA0, sW0);
+    store_scales(0);
+    sync_stage();
 
-    const int arow = wm * 64 + (lane & 31);     // + 32*ti
-    const int wrow = wn * 64 + (lane & 31);     // + 32*tj
-    const int koff = 16 * (lane >> 5);          // lane's 16 bytes of a 32-block
+    // Fragment reads: tile row 32t + lane%32 of the wave's 64-row half,
+    // logical chunk 2kb + lane/32 (the lane's 16 bytes of K block kb).
+    const int lr = lane & 31;
+    const i32x16 zero = {};
 
-    for (uint32_t st = 0; st < nst; ++st) {
-        const int buf = st & 1;
+    auto stage = [&](uint32_t st, int buf, const uint8_t *ca, const uint8_t *cw, uint8_t *na,
+                     uint8_t *nw) {
+        // the stage's scales, read before the next stage's DMA is issued
+        f32x4 asv[2], wsv;
+        if constexpr (!PARTIALS) {
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+                asv[ti] = *reinterpret_cast<const f32x4 *>(&sAs[buf][wm * 64 + 32 * ti + (lane & 31)][0]);
+            wsv = *reinterpret_cast<const f32x4 *>(&sWs[buf][wn * 64 + lane][0]);
+        }
         if (st + 1 < nst)
-            load_stage(st + 1);
+            load_stage(st + 1, na, nw);
 
-        // two K blocks at a time: a full unroll keeps every block's int32
-        // tile live at once and spills
-#pragma unroll 2
-        for (int kb = 0; kb < I8_KB; ++kb) {
-            i32x4 fa[2], fw[2];
+        // K blocks two at a time (a full unroll runs out of registers):
+        // block kb = 2*kp + h takes scale component h, and the upper two
+        // components move down after each pair
+#pragma unroll 1
+        for (int kp = 0; kp < I8_KB / 2; ++kp) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                fa[t] = *reinterpret_cast<const i32x4 *>(&sA[buf][(arow + 32 * t) * I8_PITCH + kb * 32 + koff]);
-                fw[t] = *reinterpret_cast<const i32x4 *>(&sW[buf][(wrow + 32 * t) * I8_PITCH + kb * 32 + koff]);
-            }
-            const i32x16 zero = {};
-            if constexpr (PARTIALS) {
-                uint32_t gb = st * I8_KB + kb;
+            for (int h = 0; h < 2; ++h) {
+                const int kb = 2 * kp + h;
+                const uint32_t lofs = lr * I8_BK + 16 * swz(lr, 2 * kb + (lane >> 5));
+                i32x4 fa[2], fw[2];
 #pragma unroll
-                for (int ti = 0; ti < 2; ++ti)
+                for (int t = 0; t < 2; ++t) {
+                    fa[t] = *reinterpret_cast<const i32x4 *>(&ca[(wm * 64 + 32 * t) * I8_BK + lofs]);
+                    fw[t] = *reinterpret_cast<const i32x4 *>(&cw[(wn * 64 + 32 * t) * I8_BK + lofs]);
+                }
+                if constexpr (PARTIALS) {
+                    uint32_t gb = st * I8_KB + kb;
 #pragma unroll
-                    for (int tj = 0; tj < 2; ++tj) {
-                        i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ti], fw[tj], zero, 0, 0, 0);
-                        uint32_t gj = n0 + wn * 64 + 32 * tj + (lane & 31);
+                    for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            uint32_t gi = m0 + wm * 64 + 32 * ti + mfma32_row(r, lane);
-                            if (gb < nb && gi < M && gj < N)
-                                part[((size_t)gi * N + gj) * nb + gb] = p[r];
+                        for (int tj = 0; tj < 2; ++tj) {
+                            i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ti], fw[tj], zero, 0, 0, 0);
+                            uint32_t gj = n0 + wn * 64 + 32 * tj + (lane & 31);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                uint32_t gi = m0 + wm * 64 + 32 * ti + mfma32_row(r, lane);
+                                if (gb < nb && gi < M && gj < N)
+                                    part[((size_t)gi * N + gj) * nb + gb] = p[r];
+                            }
                         }
-                    }
-            } else {
-                // scale-and-add: acc += float(P) * (a_scale[row] * w_scale[col])
-                float wsc[2];
-#pragma unroll
-                for (int tj = 0; tj < 2; ++tj)
-                    wsc[tj] = sWs[buf][kb][wn * 64 + 32 * tj + (lane & 31)];
-#pragma unroll
-                for (int ti = 0; ti < 2; ++ti) {
-                    // rows 8g + 4*(lane/32) + 0..3 of this 32-row tile, g = 0..3
-                    f32x4 asc[4];
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        asc[g] = *reinterpret_cast<const f32x4 *>(
-                            &sAs[buf][kb][wm * 64 + 32 * ti + 8 * g + 4 * (lane >> 5)]);
-#pragma unroll
-                    for (int tj = 0; tj < 2; ++tj) {
-                        i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ti], fw[tj], zero, 0, 0, 0);
+                } else {
+                    // scale-and-add: acc += float(P) * (a_scale[row] * w_scale[col]).
+                    // The scale products of one 32-row tile against both of the
+                    // wave's 32-column tiles are two 32x32 outer products, which
+                    // one v_mfma_f32_32x32x1_2b_f32 forms (block 0: columns of
+                    // tile tj = 0, block 1: tj = 1) in the register layout of the
+                    // int32 tile, each product rounded as a plain f32 multiply
+                    // rounds it.  That leaves two VALU operations per output and
+                    // K block (convert, FMA).  The second row tile's MFMAs are
+                    // issued ahead of the first tile's fold so the matrix core
+                    // runs under the VALU work.
+                    const float wsc = wsv[h];
+                    const float asc[2] = {asv[0][h], asv[1][h]};
+                    auto fold = [&](const i32x16 &p, const f32x32 &sc, int half, f32x16 &c) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            acc[ti][tj][r] = __builtin_fmaf((float)p[r], asc[r >> 2][r & 3] * wsc[tj],
-                                                            acc[ti][tj][r]);
-                    }
+                            c[r] = __builtin_fmaf((float)p[r], sc[16 * half + r], c[r]);
+                    };
+                    const f32x32 s0 = __builtin_amdgcn_mfma_f32_32x32x1f32(asc[0], wsc, f32x32{}, 0, 0, 0);
+                    const i32x16 p00 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fw[0], zero, 0, 0, 0);
+                    const i32x16 p01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fw[1], zero, 0, 0, 0);
+                    const f32x32 s1 = __builtin_amdgcn_mfma_f32_32x32x1f32(asc[1], wsc, f32x32{}, 0, 0, 0);
+                    fold(p00, s0, 0, acc[0][0]);
+                    const i32x16 p10 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[1], fw[0], zero, 0, 0, 0);
+                    fold(p01, s0, 1, acc[0][1]);
+                    const i32x16 p11 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[1], fw[1], zero, 0, 0, 0);
+                    fold(p10, s1, 0, acc[1][0]);
+                    fold(p11, s1, 1, acc[1][1]);
                 }
+            }
+            if constexpr (!PARTIALS) {
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti)
+                    asv[ti] = asv[ti].zwzw;
+                wsv = wsv.zwzw;
             }
         }
 
         if (st + 1 < nst)
-            store_stage(buf ^ 1);
-        __syncthreads();
+            store_scales(buf ^ 1);
+        sync_stage();
+    };
+    for (uint32_t st = 0; st < nst; st += 2) {
+        stage(st, 0, sA0, sW0, sA1, sW1);
+        if (st + 1 < nst)
+            stage(st + 1, 1, sA1, sW1, sA0, sW0);
     }
 
     if constexpr (!PARTIALS) {
