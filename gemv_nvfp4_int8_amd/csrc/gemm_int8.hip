@@ -28,33 +28,37 @@ constexpr int I8_KB = I8_BK / 32;                       // K blocks per stage
 constexpr int I8_SLOT = I8_BM * I8_BK;                  // one operand stage, 16 KB
 
 // DMA one operand stage: rows row0 .. row0+127 (clamped to nrows-1), bytes
-// k0 .. k0+127 of each row, into a 16 KB slot.  Rows are 128 bytes,
-// unpadded, with the 16-byte chunks XOR-swizzled as in swz(): instruction j
-// of wave w fills kilobyte 4w+j = rows 8(4w+j) .. +7, lane i landing in row
-// i/8, physical chunk i%8, which holds logical chunk (i%8) ^ swz.  A chunk
-// past the end of K (only in the last stage when K % 128 != 0) is loaded
-// from the row's first chunk instead: its K block has zero scales, so it
-// adds exactly zero, and the load stays in bounds.
-__device__ __forceinline__ void i8_dma_stage(const int8_t *__restrict__ base, uint32_t K,
+// k0 .. k0+127 of each row, into a 16 KB slot, by 16-byte buffer loads to
+// LDS (32-bit offsets from the operand's buffer resource).  Rows are 128
+// bytes, unpadded, with the 16-byte chunks XOR-swizzled as in swz():
+// instruction j of wave w fills kilobyte 2w+j = rows 8(2w+j) .. +7, lane i
+// landing in row i/8, physical chunk i%8, which holds logical chunk
+// (i%8) ^ swz.  A chunk past the end of K (only in the last stage when
+// K % 128 != 0) is loaded from the row's first chunk instead: its K block has
+// zero scales, so it adds exactly zero.
+__device__ __forceinline__ void i8_dma_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t K,
                                              uint32_t row0, uint32_t nrows, uint32_t k0,
                                              uint8_t *slot)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int kbyte = 4 * wave + j;
+    for (int j = 0; j < 2; ++j) {
+        const int kbyte = 2 * wave + j;
         const int row = 8 * kbyte + (lane >> 3);
         uint32_t gr = row0 + row;
         gr = gr < nrows ? gr : nrows - 1;
         uint32_t gk = k0 + 16u * (uint32_t)swz(row, lane & 7);
         gk = gk < K ? gk : 0u;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(base) + (size_t)gr * K + gk,
-                                         (lds_void *)(slot + 1024 * kbyte), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(slot + 1024 * kbyte), 16,
+                                                 gr * K + gk, 0, 0, 0);
     }
 }
 
+// Eight waves per 128x128 tile, each 64 rows x 32 columns (two 32x32 int32
+// tiles).  Four waves per SIMD hide each other's MFMA and LDS latencies,
+// which the fold cannot hide inside one wave in 128 VGPRs.
 template <bool PARTIALS>
-__global__ __launch_bounds__(256) void k_int8_gemm(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_int8_gemm(
     const int8_t *__restrict__ A, const int8_t *__restrict__ W,
     const float *__restrict__ as, const float *__restrict__ ws,
     uint16_t *__restrict__ out, int32_t *__restrict__ part,
@@ -74,33 +78,35 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
     tile_coords(mtiles, ntiles, tm, tn);
     const uint32_t m0 = tm * I8_BM, n0 = tn * I8_BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 1, wn = wave >> 1;      // 64-row half, 32-column quarter
     const uint32_t nb = K / 32;
     const uint32_t nst = (K + I8_BK - 1) / I8_BK;
 
-    float ras[2], rws[2];   // 512 scale values per operand per stage / 256 threads
+    // Buffer resources: every load below takes a 32-bit offset (the launch
+    // checks M*K, N*K < 2^31), and a scale offset past the end reads zero.
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)W, 0, N * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ras_r = __builtin_amdgcn_make_buffer_rsrc((void *)as, 0, M * nb * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rws_r = __builtin_amdgcn_make_buffer_rsrc((void *)ws, 0, N * nb * 4, 0x00020000);
+    constexpr uint32_t OOB = 0x80000000u;
+
+    float ras, rws;         // 512 scale values per operand per stage / 512 threads
+    // the scale loads go first, so that nothing waits on the DMA behind them
     auto load_stage = [&](uint32_t kst, uint8_t *la, uint8_t *lw) {
-        i8_dma_stage(A, K, m0, M, kst * I8_BK, la);
-        i8_dma_stage(W, K, n0, N, kst * I8_BK, lw);
         if constexpr (!PARTIALS) {      // the partials export has no scales
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                int c = threadIdx.x + 256 * j;
-                int row = c / I8_KB, b = c % I8_KB;
-                uint32_t gb = kst * I8_KB + b;
-                ras[j] = (m0 + row < M && gb < nb) ? as[(size_t)(m0 + row) * nb + gb] : 0.0f;
-                rws[j] = (n0 + row < N && gb < nb) ? ws[(size_t)(n0 + row) * nb + gb] : 0.0f;
-            }
+            const uint32_t row = threadIdx.x / I8_KB, gb = kst * I8_KB + threadIdx.x % I8_KB;
+            const uint32_t oa = (m0 + row < M && gb < nb) ? 4 * ((m0 + row) * nb + gb) : OOB;
+            const uint32_t ow = (n0 + row < N && gb < nb) ? 4 * ((n0 + row) * nb + gb) : OOB;
+            ras = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ras_r, oa, 0, 0));
+            rws = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws_r, ow, 0, 0));
         }
+        i8_dma_stage(ra, K, m0, M, kst * I8_BK, la);
+        i8_dma_stage(rw, K, n0, N, kst * I8_BK, lw);
     };
     auto store_scales = [&](int buf) {
         if constexpr (!PARTIALS) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                int c = threadIdx.x + 256 * j;
-                sAs[buf][c / I8_KB][c % I8_KB] = ras[j];
-                sWs[buf][c / I8_KB][c % I8_KB] = rws[j];
-            }
+            sAs[buf][threadIdx.x / I8_KB][threadIdx.x % I8_KB] = ras;
+            sWs[buf][threadIdx.x / I8_KB][threadIdx.x % I8_KB] = rws;
         }
     };
     // wait for this wave's DMA and LDS accesses, then for every wave's
@@ -109,33 +115,30 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
         __syncthreads();
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r)
+            acc[i][r] = 0.0f;
 
     load_stage(0, sA0, sW0);
     store_scales(0);
     sync_stage();
 
-    // Fragment reads: tile row 32t + lane%32 of the wave's 64-row half,
-    // logical chunk 2kb + lane/32 (the lane's 16 bytes of K block kb).
+    // Fragment reads: tile row 32t + lane%32 of the wave's rows, logical
+    // chunk 2kb + lane/32 (the lane's 16 bytes of K block kb).
     const int lr = lane & 31;
     const i32x16 zero = {};
 
     auto stage = [&](uint32_t st, int buf, const uint8_t *ca, const uint8_t *cw, uint8_t *na,
                      uint8_t *nw) {
         // the stage's scales, read before the next stage's DMA is issued
-        f32x4 asv[2], wsv;
+        // (lane l: a_scale of row 64wm + l, w_scale of column 32wn + l%32)
+        f32x4 asv, wsv;
         if constexpr (!PARTIALS) {
-#pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
-                asv[ti] = *reinterpret_cast<const f32x4 *>(&sAs[buf][wm * 64 + 32 * ti + (lane & 31)][0]);
-            wsv = *reinterpret_cast<const f32x4 *>(&sWs[buf][wn * 64 + lane][0]);
+            asv = *reinterpret_cast<const f32x4 *>(&sAs[buf][wm * 64 + lane][0]);
+            wsv = *reinterpret_cast<const f32x4 *>(&sWs[buf][wn * 32 + (lane & 31)][0]);
         }
         if (st + 1 < nst)
             load_stage(st + 1, na, nw);
@@ -149,61 +152,45 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
             for (int h = 0; h < 2; ++h) {
                 const int kb = 2 * kp + h;
                 const uint32_t lofs = lr * I8_BK + 16 * swz(lr, 2 * kb + (lane >> 5));
-                i32x4 fa[2], fw[2];
+                i32x4 fa[2];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < 2; ++t)
                     fa[t] = *reinterpret_cast<const i32x4 *>(&ca[(wm * 64 + 32 * t) * I8_BK + lofs]);
-                    fw[t] = *reinterpret_cast<const i32x4 *>(&cw[(wn * 64 + 32 * t) * I8_BK + lofs]);
-                }
+                const i32x4 fw = *reinterpret_cast<const i32x4 *>(&cw[wn * 32 * I8_BK + lofs]);
                 if constexpr (PARTIALS) {
                     uint32_t gb = st * I8_KB + kb;
+                    const uint32_t gj = n0 + wn * 32 + (lane & 31);
 #pragma unroll
-                    for (int ti = 0; ti < 2; ++ti)
+                    for (int ti = 0; ti < 2; ++ti) {
+                        i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ti], fw, zero, 0, 0, 0);
 #pragma unroll
-                        for (int tj = 0; tj < 2; ++tj) {
-                            i32x16 p = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ti], fw[tj], zero, 0, 0, 0);
-                            uint32_t gj = n0 + wn * 64 + 32 * tj + (lane & 31);
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                uint32_t gi = m0 + wm * 64 + 32 * ti + mfma32_row(r, lane);
-                                if (gb < nb && gi < M && gj < N)
-                                    part[((size_t)gi * N + gj) * nb + gb] = p[r];
-                            }
+                        for (int r = 0; r < 16; ++r) {
+                            uint32_t gi = m0 + wm * 64 + 32 * ti + mfma32_row(r, lane);
+                            if (gb < nb && gi < M && gj < N)
+                                part[((size_t)gi * N + gj) * nb + gb] = p[r];
                         }
+                    }
                 } else {
                     // scale-and-add: acc += float(P) * (a_scale[row] * w_scale[col]).
-                    // The scale products of one 32-row tile against both of the
-                    // wave's 32-column tiles are two 32x32 outer products, which
-                    // one v_mfma_f32_32x32x1_2b_f32 forms (block 0: columns of
-                    // tile tj = 0, block 1: tj = 1) in the register layout of the
-                    // int32 tile, each product rounded as a plain f32 multiply
-                    // rounds it.  That leaves two VALU operations per output and
-                    // K block (convert, FMA).  The second row tile's MFMAs are
-                    // issued ahead of the first tile's fold so the matrix core
-                    // runs under the VALU work.
-                    const float wsc = wsv[h];
-                    const float asc[2] = {asv[0][h], asv[1][h]};
-                    auto fold = [&](const i32x16 &p, const f32x32 &sc, int half, f32x16 &c) {
+                    // The scale products of the wave's two 32x32 tiles are two
+                    // outer products, which one v_mfma_f32_32x32x1_2b_f32 forms
+                    // (block 0: row tile 0, block 1: row tile 1) in the register
+                    // layout of the int32 tiles, each product rounded as a plain
+                    // f32 multiply rounds it.  That leaves two VALU operations
+                    // per output and K block (convert, FMA).
+                    const f32x32 sc = __builtin_amdgcn_mfma_f32_32x32x1f32(asv[h], wsv[h], f32x32{}, 0, 0, 0);
+                    const i32x16 p0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fw, zero, 0, 0, 0);
+                    const i32x16 p1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[1], fw, zero, 0, 0, 0);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            c[r] = __builtin_fmaf((float)p[r], sc[16 * half + r], c[r]);
-                    };
-                    const f32x32 s0 = __builtin_amdgcn_mfma_f32_32x32x1f32(asc[0], wsc, f32x32{}, 0, 0, 0);
-                    const i32x16 p00 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fw[0], zero, 0, 0, 0);
-                    const i32x16 p01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fw[1], zero, 0, 0, 0);
-                    const f32x32 s1 = __builtin_amdgcn_mfma_f32_32x32x1f32(asc[1], wsc, f32x32{}, 0, 0, 0);
-                    fold(p00, s0, 0, acc[0][0]);
-                    const i32x16 p10 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[1], fw[0], zero, 0, 0, 0);
-                    fold(p01, s0, 1, acc[0][1]);
-                    const i32x16 p11 = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[1], fw[1], zero, 0, 0, 0);
-                    fold(p10, s1, 0, acc[1][0]);
-                    fold(p11, s1, 1, acc[1][1]);
+                    for (int r = 0; r < 16; ++r)
+                        acc[0][r] = __builtin_fmaf((float)p0[r], sc[r], acc[0][r]);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[1][r] = __builtin_fmaf((float)p1[r], sc[16 + r], acc[1][r]);
                 }
             }
             if constexpr (!PARTIALS) {
-#pragma unroll
-                for (int ti = 0; ti < 2; ++ti)
-                    asv[ti] = asv[ti].zwzw;
+                asv = asv.zwzw;
                 wsv = wsv.zwzw;
             }
         }
@@ -219,17 +206,14 @@ __global__ __launch_bounds__(256) void k_int8_gemm(
     }
 
     if constexpr (!PARTIALS) {
+        const uint32_t gj = n0 + wn * 32 + (lane & 31);
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 2; ++tj) {
-                uint32_t gj = n0 + wn * 64 + 32 * tj + (lane & 31);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    uint32_t gi = m0 + wm * 64 + 32 * ti + mfma32_row(r, lane);
-                    if (gi < M && gj < N)
-                        out[(size_t)gi * N + gj] = (uint16_t)f32_to_bf16(acc[ti][tj][r]);
-                }
+            for (int r = 0; r < 16; ++r) {
+                uint32_t gi = m0 + wm * 64 + 32 * ti + mfma32_row(r, lane);
+                if (gi < M && gj < N)
+                    out[(size_t)gi * N + gj] = (uint16_t)f32_to_bf16(acc[ti][r]);
             }
     }
 }
@@ -239,7 +223,7 @@ hipError_t launch_int8_gemm(const int8_t *a, const int8_t *w, const float *as,
                             uint32_t m, uint32_t n, uint32_t k, hipStream_t st)
 {
     uint32_t mt = (m + I8_BM - 1) / I8_BM, nt = (n + I8_BN - 1) / I8_BN;
-    dim3 grid(mt * nt), block(256);
+    dim3 grid(mt * nt), block(512);
     if (partials)
         hipLaunchKernelGGL(k_int8_gemm<true>, grid, block, 0, st, a, w, as, ws,
                            out, partials, m, n, k, mt, nt);
