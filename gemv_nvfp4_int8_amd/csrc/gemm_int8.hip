@@ -27,33 +27,6 @@ constexpr int I8_BM = 128, I8_BN = 128, I8_BK = 128;   // BK in bytes = elements
 constexpr int I8_KB = I8_BK / 32;                       // K blocks per stage
 constexpr int I8_SLOT = I8_BM * I8_BK;                  // one operand stage, 16 KB
 
-// DMA one operand stage: rows row0 .. row0+127 (clamped to nrows-1), bytes
-// k0 .. k0+127 of each row, into a 16 KB slot, by 16-byte buffer loads to
-// LDS (32-bit offsets from the operand's buffer resource).  Rows are 128
-// bytes, unpadded, with the 16-byte chunks XOR-swizzled as in swz():
-// instruction j of wave w fills kilobyte 2w+j = rows 8(2w+j) .. +7, lane i
-// landing in row i/8, physical chunk i%8, which holds logical chunk
-// (i%8) ^ swz.  A chunk past the end of K (only in the last stage when
-// K % 128 != 0) is loaded from the row's first chunk instead: its K block has
-// zero scales, so it adds exactly zero.
-__device__ __forceinline__ void i8_dma_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t K,
-                                             uint32_t row0, uint32_t nrows, uint32_t k0,
-                                             uint8_t *slot)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int kbyte = 2 * wave + j;
-        const int row = 8 * kbyte + (lane >> 3);
-        uint32_t gr = row0 + row;
-        gr = gr < nrows ? gr : nrows - 1;
-        uint32_t gk = k0 + 16u * (uint32_t)swz(row, lane & 7);
-        gk = gk < K ? gk : 0u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(slot + 1024 * kbyte), 16,
-                                                 gr * K + gk, 0, 0, 0);
-    }
-}
-
 // Eight waves per 128x128 tile, each 64 rows x 32 columns (two 32x32 int32
 // tiles).  Four waves per SIMD hide each other's MFMA and LDS latencies,
 // which the fold cannot hide inside one wave in 128 VGPRs.
@@ -82,31 +55,58 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     const uint32_t nb = K / 32;
     const uint32_t nst = (K + I8_BK - 1) / I8_BK;
 
-    // Buffer resources: every load below takes a 32-bit offset (the launch
-    // checks M*K, N*K < 2^31), and a scale offset past the end reads zero.
+    // Buffer resources: every load below takes a 32-bit offset and is
+    // range-checked, so no load can fault.  Rows past M or N are not clamped:
+    // whatever they load feeds only accumulators that are never stored.
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, M * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void *)W, 0, N * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t ras_r = __builtin_amdgcn_make_buffer_rsrc((void *)as, 0, M * nb * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t rws_r = __builtin_amdgcn_make_buffer_rsrc((void *)ws, 0, N * nb * 4, 0x00020000);
     constexpr uint32_t OOB = 0x80000000u;
 
-    float ras, rws;         // 512 scale values per operand per stage / 512 threads
+    // Operand stages go global -> LDS by 16-byte buffer loads to LDS.  A
+    // 16 KB slot holds 128 rows of 128 bytes, unpadded, the 16-byte chunks
+    // XOR-swizzled as in swz(); instruction j of wave w fills kilobyte 2w+j =
+    // rows 16w + 8j + lane/8, lane i landing in physical chunk i%8, which
+    // holds logical chunk (i%8) ^ swz(row) = (i%8) ^ ((4j + i/16) % 8).  The
+    // lane part of the source offset takes two values (j even / odd), the
+    // rest is uniform.  A chunk past the end of K (only in the last stage
+    // when K % 128 != 0) holds whatever lies there: its K block has zero
+    // scales, so it adds exactly zero.
+    uint32_t dlane[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        dlane[j] = (uint32_t)(lane >> 3) * K + 16u * ((lane & 7) ^ ((4 * j + (lane >> 4)) & 7));
+    const uint32_t wrow = 16u * __builtin_amdgcn_readfirstlane(wave);
+    auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t row0, uint32_t k0, uint8_t *slot) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (lds_void *)(slot + 1024 * (2 * (wrow / 16) + j)), 16,
+                dlane[j] + (row0 + wrow + 8 * j) * K + k0, 0, 0, 0);
+    };
+
+    // scales: thread t loads K block t%4 of the stage for row t/4 of each
+    // operand; a block past the end of K reads zero
+    const uint32_t srow = threadIdx.x / I8_KB, sb = threadIdx.x % I8_KB;
+    const uint32_t soff_a = 4 * ((m0 + srow) * nb + sb), soff_w = 4 * ((n0 + srow) * nb + sb);
+    float ras, rws;
     // the scale loads go first, so that nothing waits on the DMA behind them
     auto load_stage = [&](uint32_t kst, uint8_t *la, uint8_t *lw) {
         if constexpr (!PARTIALS) {      // the partials export has no scales
-            const uint32_t row = threadIdx.x / I8_KB, gb = kst * I8_KB + threadIdx.x % I8_KB;
-            const uint32_t oa = (m0 + row < M && gb < nb) ? 4 * ((m0 + row) * nb + gb) : OOB;
-            const uint32_t ow = (n0 + row < N && gb < nb) ? 4 * ((n0 + row) * nb + gb) : OOB;
-            ras = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ras_r, oa, 0, 0));
-            rws = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rws_r, ow, 0, 0));
+            const bool live = kst * I8_KB + sb < nb;
+            ras = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                ras_r, live ? soff_a + 16 * kst : OOB, 0, 0));
+            rws = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rws_r, live ? soff_w + 16 * kst : OOB, 0, 0));
         }
-        i8_dma_stage(ra, K, m0, M, kst * I8_BK, la);
-        i8_dma_stage(rw, K, n0, N, kst * I8_BK, lw);
+        dma(ra, m0, kst * I8_BK, la);
+        dma(rw, n0, kst * I8_BK, lw);
     };
     auto store_scales = [&](int buf) {
         if constexpr (!PARTIALS) {
-            sAs[buf][threadIdx.x / I8_KB][threadIdx.x % I8_KB] = ras;
-            sWs[buf][threadIdx.x / I8_KB][threadIdx.x % I8_KB] = rws;
+            sAs[buf][srow][sb] = ras;
+            sWs[buf][srow][sb] = rws;
         }
     };
     // wait for this wave's DMA and LDS accesses, then for every wave's
@@ -127,8 +127,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     sync_stage();
 
     // Fragment reads: tile row 32t + lane%32 of the wave's rows, logical
-    // chunk 2kb + lane/32 (the lane's 16 bytes of K block kb).
+    // chunk 2kb + lane/32 (the lane's 16 bytes of K block kb), i.e. physical
+    // chunk (lane/32 ^ s) ^ 2kb with s = ((lane%32) >> 1) % 8.  Block kb's
+    // offset is the block-0 offset XOR 32kb (the slot base is 1 KB aligned).
     const int lr = lane & 31;
+    const uint32_t fofs = lr * I8_BK + 16 * ((lane >> 5) ^ ((lr >> 1) & 7));
+    const uint32_t fa_ofs = wm * 64 * I8_BK + fofs, fw_ofs = wn * 32 * I8_BK + fofs;
     const i32x16 zero = {};
 
     auto stage = [&](uint32_t st, int buf, const uint8_t *ca, const uint8_t *cw, uint8_t *na,
@@ -151,12 +155,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int kb = 2 * kp + h;
-                const uint32_t lofs = lr * I8_BK + 16 * swz(lr, 2 * kb + (lane >> 5));
+                const uint32_t ao = fa_ofs ^ (32u * kb), wo = fw_ofs ^ (32u * kb);
                 i32x4 fa[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    fa[t] = *reinterpret_cast<const i32x4 *>(&ca[(wm * 64 + 32 * t) * I8_BK + lofs]);
-                const i32x4 fw = *reinterpret_cast<const i32x4 *>(&cw[wn * 32 * I8_BK + lofs]);
+                    fa[t] = *reinterpret_cast<const i32x4 *>(&ca[ao + 32 * t * I8_BK]);
+                const i32x4 fw = *reinterpret_cast<const i32x4 *>(&cw[wo]);
                 if constexpr (PARTIALS) {
                     uint32_t gb = st * I8_KB + kb;
                     const uint32_t gj = n0 + wn * 32 + (lane & 31);
