@@ -114,16 +114,24 @@ def abi_version() -> int:
 
 
 # ------------------------------------------------------------------ helpers
+# torch's current stream of the current device, as a raw handle.  The
+# private accessor costs ~0.1 us against ~2.7 us for building a Stream object
+# (per-call overhead matters: a narrow GEMV runs in a few microseconds).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
     if stream is None:
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if _raw_stream is not None:
+            return _raw_stream(torch._C._cuda_getDevice())
+        return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
-        return ctypes.c_void_p(stream.cuda_stream)
-    return ctypes.c_void_p(int(stream))
+        return stream.cuda_stream
+    return int(stream)
 
 
 def _ptr(t: torch.Tensor):
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _need(t: torch.Tensor, name: str, dtypes, shape):
@@ -135,7 +143,7 @@ def _need(t: torch.Tensor, name: str, dtypes, shape):
         raise ValueError(f"{name}: must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
 
 

@@ -273,10 +273,12 @@ def test_fp8_gemv_batched_rows_bit_identical_to_single_row(n, k):
         assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
 
 
-@pytest.mark.parametrize("n,k", [(70000, 512), (65552, 1040), (37, 1040)])
+@pytest.mark.parametrize("n,k", [(70000, 512), (65552, 1040), (37, 1040), (12300, 1040)])
 def test_fp8_gemv_wide_and_partial_segments(n, k):
     # n >= 65536 takes the row-split kernel; k = 1040 ends 16 elements into a
-    # 256-element segment; n = 70000 / 65552 leave ragged row tiles.
+    # 256-element segment; n = 70000 / 65552 leave ragged row tiles; n = 12300
+    # takes the K-split kernel with two segments in flight, ragged against
+    # both its 8- and 16-row units, and its last wave gets no segment.
     w = synth.gemv_weight_bf16(n, k, "cpu", shape_id=2)
     ow, ows = oracle.quant_rowwise_fp8(bits(w))
     wq, ws = dev(torch.from_numpy(ow)), dev(torch.from_numpy(ows))
@@ -290,10 +292,11 @@ def test_fp8_gemv_wide_and_partial_segments(n, k):
 # ---------------------------------------------------------------------------
 # Block-scaled FP8 GEMV (fp8_gemv_batch.rs, w8a16_gemv_batch4 / _batch2).
 @pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 1152), (6144, 5120),
-                                 (65664, 640)])
+                                 (12416, 1152), (65664, 640)])
 def test_fp8_gemv_blockscale_all_m(n, k):
     # k = 384 and 1152 end half-way through a 256-element segment; k = 1152
-    # leaves the last K-split wave without a segment; n = 65664 takes the
+    # leaves the last K-split wave without a segment; n = 12416 takes the
+    # K-split kernel with two segments in flight; n = 65664 takes the
     # row-split kernel.
     w, grid = synth.gemv_block_weight(n, k, "cpu", shape_id=0)
     x = synth.gemv_acts_bf16(16, k, "cpu", shape_id=3)
