@@ -215,3 +215,95 @@ def test_w4a4_tile_order_must_be_known():
                                  None) == qp.QP_ERR_FORMAT
     assert L.w4a4_gemm_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 64, 64, 48,
                              qp.QP_TILES_NFAST, None) == qp.QP_ERR_SHAPE
+
+
+def _pp():
+    return ctypes.byref(ctypes.c_void_p())
+
+
+# Every stateless entry point with fake (never dereferenced) pointers and
+# sizes that pass every check; each case zeroes one extent.
+_EXTENT_CALLS = {
+    "requant_w_nvfp4_int8": (lambda n, k: L.requant_w_nvfp4_int8(
+        FAKE, FAKE2, 1.0, FAKE, FAKE2, n, k, None), (256, 256)),
+    "requant_a_bf16_int8": (lambda m, k: L.requant_a_bf16_int8(
+        FAKE, FAKE2, FAKE, m, k, None), (4, 256)),
+    "int8_gemm_blockscaled": (lambda m, n, k: L.int8_gemm_blockscaled(
+        FAKE, FAKE2, FAKE, FAKE2, FAKE, m, n, k, None), (4, 256, 256)),
+    "int8_w4a8_prefill": (lambda m, n, k: L.int8_w4a8_prefill(
+        FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
+    "int8_gemm_block_partials": (lambda m, n, k: L.int8_gemm_block_partials(
+        FAKE, FAKE2, FAKE, m, n, k, None), (4, 256, 256)),
+    "quantize_bf16_nvfp4": (lambda r, k: L.quantize_bf16_nvfp4(
+        FAKE, FAKE2, FAKE, 1.0, r, k, None), (4, 256)),
+    "w4a4_gemm": (lambda m, n, k: L.w4a4_gemm(
+        FAKE, FAKE2, FAKE, FAKE2, FAKE, 1.0, 1.0, m, n, k, None), (4, 256, 256)),
+    "w4a4_gemm_tiles": (lambda m, n, k: L.w4a4_gemm_tiles(
+        FAKE, FAKE2, FAKE, FAKE2, FAKE, 1.0, 1.0, m, n, k, qp.QP_TILES_BANDED, None),
+        (4, 256, 256)),
+    "requant_w_blockfp8_rowwise": (lambda n, k: L.requant_w_blockfp8_rowwise(
+        qp.QP_FP8_BLOCK128, FAKE, FAKE2, FAKE, FAKE2, _pp(), _pp(), n, k, None), (256, 256)),
+    "quant_rowwise_fp8": (lambda r, k: L.quant_rowwise_fp8(
+        FAKE, FAKE2, FAKE, r, k, None), (4, 256)),
+    "fp8_gemm_rowscale": (lambda m, n, k: L.fp8_gemm_rowscale(
+        FAKE, FAKE2, FAKE, FAKE2, FAKE, m, n, k, None), (4, 256, 256)),
+    "fp8_rowwise_proj": (lambda m, n, k: L.fp8_rowwise_proj(
+        qp.QP_FP8_PER_ROW, FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE2, m, n, k, None),
+        (4, 256, 256)),
+    "fp8_gemv_rowscale": (lambda m, n, k: L.fp8_gemv_rowscale(
+        FAKE, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
+    "fp8_gemv_blockscale": (lambda m, n, k: L.fp8_gemv_blockscale(
+        FAKE, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
+    "w4a16_gemv": (lambda m, n, k: L.w4a16_gemv(
+        FAKE, FAKE2, FAKE, 1.0, FAKE2, m, n, k, None), (4, 256, 256)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_EXTENT_CALLS))
+def test_empty_extent_is_rejected_before_any_launch(name):
+    """A zero M, N, K or row count is an error (QP_ERR_SHAPE, or QP_ERR_RANGE
+    where M has a documented range), returned by the host checks: the
+    launch counter does not move."""
+    call, sizes = _EXTENT_CALLS[name]
+    for i in range(len(sizes)):
+        args = list(sizes)
+        args[i] = 0
+        before = qp.launch_count()
+        st = call(*args)
+        assert st in (qp.QP_ERR_SHAPE, qp.QP_ERR_RANGE), (name, args, st)
+        assert qp.launch_count() == before
+
+
+def test_every_stateless_entry_point_is_in_the_extent_table():
+    stateless = [n for n in _declared_functions()
+                 if not n.startswith("qproj_") and not n.endswith("_cached")]
+    assert sorted(stateless) == sorted(_EXTENT_CALLS)
+
+
+def test_empty_extent_is_rejected_by_the_cached_entry_points():
+    h = ctypes.c_void_p()
+    assert L.qproj_cache_create(ctypes.byref(h)) == qp.QP_OK
+    try:
+        calls = [
+            (lambda n, k: L.requant_w_blockfp8_rowwise_cached(
+                h, qp.QP_FP8_BLOCK128, FAKE, FAKE2, n, k, _pp(), _pp(), None), (256, 256)),
+            (lambda n, k: L.requant_w_nvfp4_int8_cached(
+                h, FAKE, FAKE2, 1.0, n, k, _pp(), _pp(), None), (256, 256)),
+            (lambda m, n, k: L.fp8_rowwise_proj_cached(
+                h, qp.QP_FP8_BLOCK128, FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE2, m, n, k, None),
+             (4, 256, 256)),
+            (lambda m, n, k: L.int8_w4a8_prefill_cached(
+                h, FAKE, FAKE2, FAKE, 1.0, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
+        ]
+        for call, sizes in calls:
+            for i in range(len(sizes)):
+                args = list(sizes)
+                args[i] = 0
+                before = qp.launch_count()
+                assert call(*args) == qp.QP_ERR_SHAPE, args
+                assert qp.launch_count() == before
+        e, b = ctypes.c_uint64(), ctypes.c_uint64()
+        assert L.qproj_cache_stats(h, ctypes.byref(e), ctypes.byref(b)) == qp.QP_OK
+        assert (e.value, b.value) == (0, 0)       # nothing derived, nothing allocated
+    finally:
+        assert L.qproj_cache_destroy(h) == qp.QP_OK
