@@ -262,7 +262,9 @@ int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
         return e;
     if (m < 1 || m > 16)
         return QP_ERR_RANGE;
-    if (n == 0 || k == 0 || k % 16 != 0 || !fits(n, k) || !fits(m, n))
+    // (the K-split kernel addresses the activations with 31-bit byte offsets)
+    if (n == 0 || k == 0 || k % 16 != 0 || !fits(n, k) || !fits(m, n) ||
+        (uint64_t)2 * m * k >= (1ull << 31))
         return QP_ERR_SHAPE;
     return done(qp::launch_fp8_gemv_rowscale(x, w, row_scale, out, m, n, k, S(stream)));
 }
@@ -275,7 +277,8 @@ int fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
         return e;
     if (m < 1 || m > 16)
         return QP_ERR_RANGE;
-    if (n == 0 || k == 0 || n % 128 != 0 || k % 128 != 0 || !fits(n, k) || !fits(m, n))
+    if (n == 0 || k == 0 || n % 128 != 0 || k % 128 != 0 || !fits(n, k) || !fits(m, n) ||
+        (uint64_t)2 * m * k >= (1ull << 31))
         return QP_ERR_SHAPE;
     return done(qp::launch_fp8_gemv_blockscale(x, w, block_scale, out, m, n, k, S(stream)));
 }

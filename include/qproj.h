@@ -226,9 +226,10 @@ int fp8_rowwise_proj(int fmt, const uint8_t *w, const float *w_scale,
  *  dense_gemv_fp8w_batch2):
  *   C[i,j] = bf16( row_scale[j] * sum_t x[i,t] * e4m3(w[j,t]) ),
  *   x [m,k] BF16, w [n,k] E4M3, row_scale [n] F32, out [m,n] BF16.
- * 1 <= m <= 16 (else QP_ERR_RANGE); k % 16 == 0.  The weight is streamed
- * from memory once for all m rows, and every output row is bit-identical to
- * the m == 1 call on that row.
+ * 1 <= m <= 16 (else QP_ERR_RANGE); k % 16 == 0, n*k and m*n < 2^31 and
+ * 2*m*k < 2^31 (else QP_ERR_SHAPE).  The weight is streamed from memory
+ * once for all m rows, and every output row is bit-identical to the m == 1
+ * call on that row.
  * ---------------------------------------------------------------------- */
 int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
                       const float *row_scale, uint16_t *out, uint32_t m,
@@ -243,7 +244,8 @@ int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
  *   x [m,k] BF16, w [n,k] E4M3, block_scale [n/128, k/128] F32 row-major,
  *   out [m,n] BF16; all device memory owned by the caller, out written.
  * 1 <= m <= 16 (else QP_ERR_RANGE; the pages' batched kernels stop at 4);
- * n % 128 == 0 and k % 128 == 0 (else QP_ERR_SHAPE).  Each 128-element K
+ * n % 128 == 0, k % 128 == 0, n*k and m*n < 2^31 and 2*m*k < 2^31 (else
+ * QP_ERR_SHAPE).  Each 128-element K
  * block is summed in F32 and added to the running F32 sum with one FMA by
  * its scale; the BF16 rounding happens once at the end.  The weight is
  * streamed once for all m rows, and every output row is bit-identical to the

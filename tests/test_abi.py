@@ -307,3 +307,10 @@ def test_empty_extent_is_rejected_by_the_cached_entry_points():
         assert (e.value, b.value) == (0, 0)       # nothing derived, nothing allocated
     finally:
         assert L.qproj_cache_destroy(h) == qp.QP_OK
+
+
+def test_gemv_activation_bytes_limit():
+    # 2*m*k must stay below 2^31 (31-bit activation offsets); n*k stays legal
+    for fn in (L.fp8_gemv_rowscale, L.fp8_gemv_blockscale):
+        assert fn(FAKE, FAKE2, FAKE, FAKE2, 16, 128, 1 << 26, None) == qp.QP_ERR_SHAPE
+        assert fn(FAKE, FAKE2, FAKE, FAKE2, 8, 128, 1 << 27, None) == qp.QP_ERR_SHAPE
