@@ -15,9 +15,10 @@
 // vector ALU 4 cycles per wave instruction, against 32 cycles for the int8
 // MFMA of a whole 32x32x32 block.  It therefore keeps the VALU work per
 // output and block at two instructions (the scale product moves to the
-// matrix core) and feeds the VALU without stalls: operand stages arrive by
-// LDS-DMA, which holds no registers, so the next tile's MFMAs can be in
-// flight while the current tile is folded.
+// matrix core) and keeps the VALU fed: inside a wave each fold waits for its
+// MFMAs, so four waves share every SIMD (eight 64x32 waves per 128x128 tile,
+// two tiles per CU) and fill each other's waits.  That fits in 128 VGPRs
+// because operand stages arrive by LDS-DMA, which holds no registers.
 #include "gemm_common.hpp"
 #include "qp_launch.hpp"
 

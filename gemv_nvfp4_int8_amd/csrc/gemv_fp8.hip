@@ -30,8 +30,10 @@
 //    each wave its own rows over all of K, with the activation segment staged
 //    once per workgroup in LDS and shared by its four waves; narrow weights
 //    split K over the four waves of a workgroup (everything wave-private) and
-//    add the partial tiles in a fixed order.  No summation order depends on
-//    M, so every output row is bit-identical to an M = 1 call on that row.
+//    add the partial tiles in a fixed order.  The narrow kernel's launch
+//    shape (8 or 16 rows per workgroup, activation rows loaded, segments in
+//    flight) may follow M, but no summation order depends on M, so every
+//    output row is bit-identical to an M = 1 call on that row.
 #include "qp_device.hpp"
 #include "qp_launch.hpp"
 
