@@ -138,6 +138,24 @@ struct ScaleDiv {
     }
 };
 
+// t[i] = x[i] / d.s for N values, each correctly rounded.  One wave vote picks
+// the branch-free quotient for every value when every active lane's scale
+// allows it (the common case); otherwise each value takes operator(), whose
+// per-value branches would otherwise be paid by every call.
+template <int N>
+__device__ __forceinline__ void div_all(const ScaleDiv &d, const float *x, float *t)
+{
+    if (__all(d.fast)) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            t[i] = d.quick(x[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            t[i] = d(x[i]);
+    }
+}
+
 // Hardware converters.  Each was compared on this part with the software
 // encoders above over every binary32 input of its domain (both signs) and
 // agrees bit for bit: E4M3 for |y| <= 448 (beyond 464 the converter returns

@@ -63,9 +63,7 @@ __global__ __launch_bounds__(256) void k_requant_a_bf16_int8(
         if (sc != 0.0f) {
             ScaleDiv d(sc);
             float t[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                t[i] = d(x[i]);
+            div_all<8>(d, x, t);
             out[0] = cvt_i8x4(&t[0]);
             out[1] = cvt_i8x4(&t[4]);
         }
@@ -140,9 +138,7 @@ __global__ __launch_bounds__(256) void k_requant_w_nvfp4_int8(
         u32x4 o = {0, 0, 0, 0};
         if (sc != 0.0f) {
             ScaleDiv d(sc);
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                v[i] = d(v[i]);
+            div_all<16>(d, v, v);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 o[j] = cvt_i8x4(&v[4 * j]);
@@ -210,9 +206,7 @@ __global__ __launch_bounds__(256) void k_quantize_bf16_nvfp4(
         uint32_t codes = 0;
         if (d != 0.0f) {
             ScaleDiv dv(d);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = dv(v[i]);
+            div_all<8>(dv, v, v);
             codes = cvt_e2m1x8(v);
         }
         // scales of the blocks of lanes 8g .. 8g+7 (every other lane) -> lane 8g
@@ -277,9 +271,7 @@ __device__ __forceinline__ u32x2 enc8_e4m3(const float *v, const ScaleDiv &d, bo
     u32x2 o = {0, 0};
     if (!zero) {
         float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            t[i] = d(v[i]);
+        div_all<8>(d, v, t);
         o[0] = cvt_e4m3x4(t[0], t[1], t[2], t[3]);
         o[1] = cvt_e4m3x4(t[4], t[5], t[6], t[7]);
     }
