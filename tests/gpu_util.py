@@ -54,11 +54,12 @@ def bf16_f64(b):
 
 
 def assert_gemm_close(got_bits, ref_bits, what=""):
-    """North-star GEMM bound: max|C_gpu - C_ref| <= 1e-2 * max|C_ref| per
-    matrix.  A second, tighter bound (F32 accumulation differs from the
-    binary64 oracle only by rounding order, so nearly every element lands on
-    the same or the neighbouring BF16) guards against small systematic slips
-    that the loose bound would let through."""
+    """GEMM bound: max|C_gpu - C_ref| <= 1e-2 * max|C_ref| per matrix, the
+    tolerance stated for the block-scaled contractions.  A second, tighter
+    bound (F32 accumulation differs from the binary64 oracle only by
+    rounding order, so nearly every element lands on the same or the
+    neighbouring BF16) guards against small systematic slips that the loose
+    bound would let through."""
     g, r = bf16_f64(got_bits), bf16_f64(ref_bits)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     err = np.abs(g - r)
