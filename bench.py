@@ -515,6 +515,12 @@ def run_secondary(qp, synth, dev, only):
         del copies, wq, wsr, x, aq, asr, o
         torch.cuda.empty_cache()
 
+    # The vendor library (hipBLASLt through torch) on the GEMM shapes, for
+    # context beside the kernels above.  Run only when named in --only; it
+    # is a measurement, never part of the library's path.
+    if "vendor" in only:
+        res["vendor"] = vendor_gemms(torch, dev)
+
     # Block FP8 -> row-wise FP8 requant + row-wise FP8 GEMM, M = 8192.
     if want("fp8") or want("requant_w_blockfp8_rowwise") or want("quant_rowwise_fp8") \
             or want("fp8_gemm_rowscale"):
@@ -542,6 +548,60 @@ def run_secondary(qp, synth, dev, only):
         del c, wq, wsr, aq, asr, out
         torch.cuda.empty_cache()
     return res
+
+
+def vendor_gemms(torch, dev):
+    """hipBLASLt (torch._scaled_mm, torch._int_mm, torch.matmul) on the GEMM
+    shapes: FP8 with row-wise and tensor-wise scales on the row-scaled FP8
+    shape, plain int8 (no block scales) and BF16 on the int8 shape, BF16 and
+    tensor-scaled FP8 on the W4A4 shape.  Eager launches (library calls stay
+    out of graph capture); random operands of the same shapes."""
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+
+    def item(name, flops, fn, peak):
+        ms = time_launches(lambda i: fn(), iters=20, graph=False)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1), "peak_dtype": peak,
+                     "frac_peak": round(tf / PEAK_TFLOPS[peak], 4)}
+        log(f"  vendor {name}: {ms*1e3:.1f} us  {tf:.1f} TFLOP/s ({tf / PEAK_TFLOPS[peak]:.1%} of {peak})")
+
+    def f8(shape):
+        return (torch.randn(shape, generator=g, device=dev) * 0.5).to(torch.float8_e4m3fn)
+
+    m, n, k = 8192, 12288, 5120
+    a, w = f8((m, k)), f8((n, k))
+    sa = torch.rand((m, 1), generator=g, device=dev) + 0.5
+    sw = torch.rand((1, n), generator=g, device=dev) + 0.5
+    one = torch.ones((), device=dev)
+    item("fp8_rowwise_8192x12288x5120", 2 * m * n * k,
+         lambda: torch._scaled_mm(a, w.t(), sa, sw, out_dtype=torch.bfloat16), "fp8")
+    item("fp8_tensorwise_8192x12288x5120", 2 * m * n * k,
+         lambda: torch._scaled_mm(a, w.t(), one, one, out_dtype=torch.bfloat16), "fp8")
+    del a, w, sa, sw
+
+    m, n, k = 2048, 17408, 5120
+    ai = torch.randint(-127, 128, (m, k), generator=g, device=dev, dtype=torch.int8)
+    wi = torch.randint(-127, 128, (n, k), generator=g, device=dev, dtype=torch.int8)
+    item("int8_plain_2048x17408x5120", 2 * m * n * k, lambda: torch._int_mm(ai, wi.t()), "int8")
+    del ai, wi
+    ab = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+    wb = torch.randn((n, k), generator=g, device=dev).to(torch.bfloat16)
+    item("bf16_2048x17408x5120", 2 * m * n * k, lambda: ab @ wb.t(), "bf16")
+    del ab, wb
+
+    m, n, k = 4096, 5120, 17408
+    ab = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+    wb = torch.randn((n, k), generator=g, device=dev).to(torch.bfloat16)
+    item("bf16_4096x5120x17408", 2 * m * n * k, lambda: ab @ wb.t(), "bf16")
+    a, w = ab.to(torch.float8_e4m3fn), wb.to(torch.float8_e4m3fn)
+    del ab, wb
+    item("fp8_tensorwise_4096x5120x17408", 2 * m * n * k,
+         lambda: torch._scaled_mm(a, w.t(), one, one, out_dtype=torch.bfloat16), "fp8")
+    del a, w
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(synth):

@@ -5,8 +5,8 @@ owned by the caller), checks their dtypes and shapes so that no kernel can
 be handed a buffer smaller than it will touch, and calls the C entry point of
 the same name with raw pointers, sizes and torch's current HIP stream.
 Every step of the computation runs in the library's HIP kernels; there is no
-fallback.  If ``libqproj.so`` has not been built, importing the library
-raises immediately (build it with ``__graft_entry__.build()`` or
+fallback.  If ``libqproj.so`` has not been built, the first call into the
+library raises ImportError (build it with ``__graft_entry__.build()`` or
 ``python -m gemv_nvfp4_int8_amd._build``).
 
 The operations and their rounding rules are documented in include/qproj.h.
