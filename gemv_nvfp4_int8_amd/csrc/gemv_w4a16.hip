@@ -262,9 +262,12 @@ constexpr int W4_GB = W4_GW * W4_SB;        // scale bytes per row per group (64
 // Wide weights, scales: the workgroup loads the scale bytes of all its rows
 // for a group of 2 windows (64 bytes per row, 8 bytes per thread) one group
 // ahead and keeps them in LDS (double-buffered), instead of each lane
-// fetching its own 2 bytes per window.
+// fetching its own 2 bytes per window.  The one-group kernel is held to five
+// waves per SIMD (<= 102 VGPRs); the two-group kernel is left to the
+// compiler, whose unconstrained schedule keeps the scale and activation
+// loads in flight across the window barrier (measured).
 template <int MG, int RG>
-__global__ __launch_bounds__(256) void k_w4a16_gemv_rows(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5 : 1))) void k_w4a16_gemv_rows(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
     const uint8_t *__restrict__ ws, float scale2, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k)
@@ -320,6 +323,24 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv_rows(
     // Scale bytes at or beyond k/16 in a row are zeroed in registers (an
     // 8-byte piece can straddle the end of a row's scales when k % 128 != 0);
     // a zero scale times a zero partial adds nothing.
+    //
+    // The range check of a buffer load zeroes every dword that reaches past
+    // the end of the buffer, in-range bytes included.  When k/16 % 4 == 2,
+    // the dword holding the matrix's last two scale bytes (the end of the
+    // last row) is such a dword, so those two bytes are loaded once on
+    // their own and put back when that piece is stashed: in dword fix_d of
+    // piece j of group fix_g[j], on the one thread that owns it.
+    const uint32_t stot = n * srow;         // scale bytes in the buffer
+    const uint32_t last2 = __builtin_amdgcn_raw_buffer_load_b16(rs, stot - 2, 0, 0);
+    uint32_t fix_g[SCH];
+    const uint32_t fix_d = ((srow - 2) % 8) / 4;
+#pragma unroll
+    for (int j = 0; j < SCH; ++j) {
+        const bool owner = srow % 4 == 2 && sso[j] < W4_OOB &&
+                           wg_row0 + ((tid + 256 * j) >> 3) == n - 1 &&
+                           (srow - 2) % W4_GB / 8 * 8 == sbo[j];
+        fix_g[j] = owner ? (srow - 2) / W4_GB : ~0u;
+    }
     auto load_sg = [&](u32x2 *v, uint32_t grp) {
 #pragma unroll
         for (int j = 0; j < SCH; ++j) {
@@ -336,11 +357,16 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv_rows(
             }
         }
     };
-    auto stash_sg = [&](const u32x2 *v, int buf) {
+    auto stash_sg = [&](const u32x2 *v, uint32_t grp, int buf) {
 #pragma unroll
-        for (int j = 0; j < SCH; ++j)
+        for (int j = 0; j < SCH; ++j) {
+            u32x2 p = v[j];
+            const uint32_t fix = grp == fix_g[j] ? last2 : 0u;
+            p[0] |= fix_d == 0 ? fix : 0u;
+            p[1] |= fix_d == 1 ? fix : 0u;
             if (tid + 256 * j < WG_ROWS * 8)
-                *reinterpret_cast<u32x2 *>(&ss[buf][slo[j]]) = v[j];
+                *reinterpret_cast<u32x2 *>(&ss[buf][slo[j]]) = p;
+        }
     };
     // a lane's fragments: row 4 g + l%4, elements 32 (l/4) + 8 i ..
     auto read_frags = [&](W4Act<MG> &a, int buf) {
@@ -388,14 +414,14 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv_rows(
     uint32_t win = 0;
     for (; win + 2 <= nwin; win += 2) {
         const int sb = (win / 2) & 1;
-        stash_sg(sg, sb);
+        stash_sg(sg, win / 2, sb);
         load_sg(sg, win / 2 + 1);
         step(A, xa, win, 0, sb, 0);
         step(B, xb, win + 1, 1, sb, 1);
     }
     if (win < nwin) {               // an odd last window, already in A
         const int sb = (win / 2) & 1;
-        stash_sg(sg, sb);
+        stash_sg(sg, win / 2, sb);
         step(A, xa, win, 0, sb, 0);
     }
     w4_block_sum<MG, RG>(acc);
