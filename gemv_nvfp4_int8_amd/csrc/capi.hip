@@ -159,7 +159,10 @@ int w4a4_gemm_tiles(const uint8_t *a_packed, const uint8_t *a_scale,
         return QP_ERR_FORMAT;
     if (!a_packed || !a_scale || !w_packed || !w_scale || !out)
         return QP_ERR_NULL;
-    if (!aligned16(a_packed) || !aligned16(w_packed) || !aligned16(out))
+    // the large-tile kernel stages scale rows with 16-byte loads, so the
+    // scale grids need the same alignment as every other pointer
+    if (!aligned16(a_packed) || !aligned16(w_packed) || !aligned16(out) ||
+        !aligned16(a_scale) || !aligned16(w_scale))
         return QP_ERR_ALIGN;
     if (m == 0 || n == 0 || k == 0 || k % 32 != 0 || !fits(m, k) ||
         !fits(n, k) || !fits(m, n))

@@ -136,7 +136,9 @@ int quantize_bf16_nvfp4(const uint16_t *x, uint8_t *packed, uint8_t *scale,
  *                  sum_b e4m3(a_scale[i,b]) * e4m3(w_scale[j,b]) * P_b ),
  *   P_b = sum_{t in 16-block b} e2m1(a[i,t]) * e2m1(w[j,t]).
  *   a_packed [m,k/2], a_scale [m,k/16], w_packed [n,k/2], w_scale [n,k/16],
- *   out [m,n] BF16.  Requires k % 32 == 0.
+ *   out [m,n] BF16.  Requires k % 32 == 0.  All five pointers 16-byte
+ *   aligned, the scale grids included (unlike quantize_bf16_nvfp4's scale
+ *   output, which needs only 2 bytes); else QP_ERR_ALIGN.
  * Each block's E4M3 scale is folded into its E2M1 operands (the product is
  * exact in FP16), so the contraction runs on FP16 MFMA with F32
  * accumulation and the per-block scaling costs no extra pass.

@@ -314,3 +314,52 @@ def test_gemv_activation_bytes_limit():
     for fn in (L.fp8_gemv_rowscale, L.fp8_gemv_blockscale):
         assert fn(FAKE, FAKE2, FAKE, FAKE2, 16, 128, 1 << 26, None) == qp.QP_ERR_SHAPE
         assert fn(FAKE, FAKE2, FAKE, FAKE2, 8, 128, 1 << 27, None) == qp.QP_ERR_SHAPE
+
+
+# Every device pointer of every stateless entry point, by position: call(p)
+# takes the list of pointer values.  Block formats are used where a format
+# tag decides which pointers are read.
+_PTR_CALLS = {
+    "requant_w_nvfp4_int8": (lambda p: L.requant_w_nvfp4_int8(
+        p[0], p[1], 1.0, p[2], p[3], 256, 256, None), 4),
+    "requant_a_bf16_int8": (lambda p: L.requant_a_bf16_int8(p[0], p[1], p[2], 4, 256, None), 3),
+    "int8_gemm_blockscaled": (lambda p: L.int8_gemm_blockscaled(
+        p[0], p[1], p[2], p[3], p[4], 4, 256, 256, None), 5),
+    "int8_w4a8_prefill": (lambda p: L.int8_w4a8_prefill(
+        p[0], p[1], p[2], p[3], p[4], p[5], 4, 256, 256, None), 6),
+    "int8_gemm_block_partials": (lambda p: L.int8_gemm_block_partials(
+        p[0], p[1], p[2], 4, 256, 256, None), 3),
+    "quantize_bf16_nvfp4": (lambda p: L.quantize_bf16_nvfp4(p[0], p[1], p[2], 1.0, 4, 256, None), 3),
+    "w4a4_gemm": (lambda p: L.w4a4_gemm(p[0], p[1], p[2], p[3], p[4], 1.0, 1.0, 4, 256, 256, None), 5),
+    "w4a4_gemm_tiles": (lambda p: L.w4a4_gemm_tiles(
+        p[0], p[1], p[2], p[3], p[4], 1.0, 1.0, 4, 256, 256, qp.QP_TILES_BANDED, None), 5),
+    "requant_w_blockfp8_rowwise": (lambda p: L.requant_w_blockfp8_rowwise(
+        qp.QP_FP8_BLOCK128, p[0], p[1], p[2], p[3], _pp(), _pp(), 256, 256, None), 4),
+    "quant_rowwise_fp8": (lambda p: L.quant_rowwise_fp8(p[0], p[1], p[2], 4, 256, None), 3),
+    "fp8_gemm_rowscale": (lambda p: L.fp8_gemm_rowscale(p[0], p[1], p[2], p[3], p[4], 4, 256, 256, None), 5),
+    "fp8_rowwise_proj": (lambda p: L.fp8_rowwise_proj(
+        qp.QP_FP8_BLOCK128, p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], 4, 256, 256, None), 8),
+    "fp8_gemv_rowscale": (lambda p: L.fp8_gemv_rowscale(p[0], p[1], p[2], p[3], 4, 256, 256, None), 4),
+    "fp8_gemv_blockscale": (lambda p: L.fp8_gemv_blockscale(p[0], p[1], p[2], p[3], 4, 256, 256, None), 4),
+    "w4a16_gemv": (lambda p: L.w4a16_gemv(p[0], p[1], p[2], 1.0, p[3], 4, 256, 256, None), 4),
+}
+
+
+def test_every_stateless_entry_point_is_in_the_pointer_table():
+    assert sorted(_PTR_CALLS) == sorted(_EXTENT_CALLS)
+
+
+@pytest.mark.parametrize("name", sorted(_PTR_CALLS))
+def test_every_pointer_is_checked_before_any_launch(name):
+    """Each device pointer, in turn, null and then one byte off its
+    alignment: QP_ERR_NULL and QP_ERR_ALIGN from the host checks, with the
+    other pointers valid and nothing launched."""
+    call, count = _PTR_CALLS[name]
+    for i in range(count):
+        for bad, want in ((0, qp.QP_ERR_NULL), (1, qp.QP_ERR_ALIGN)):
+            p = [FAKE if j % 2 == 0 else FAKE2 for j in range(count)]
+            p[i] = bad if bad == 0 else p[i] + bad
+            before = qp.launch_count()
+            st = call(p)
+            assert st == want, (name, i, bad, st)
+            assert qp.launch_count() == before
