@@ -117,12 +117,14 @@ def test_w4a16_gemv_one_output_row_and_k32(n, k):
                           f"w4a16 {n}x{k} m={m}")
 
 
-# k / 16 % 4 == 2 on the row-split kernel: the last row's last 8-byte scale
-# piece starts half a dword before the end of the scale buffer (at k = 32,
-# 160 and 2080 it starts at byte 0, 8 and 128 of the row's scales).  A load
-# that reaches past the end zeroes that whole dword, so the kernel must fetch
-# the piece from inside the buffer; the last rows carry the check.
-@pytest.mark.parametrize("n,k", [(65540, 32), (65536, 160), (65544, 2080)])
+# k / 16 % 4 == 2 on the row-split kernel: the dword holding the matrix's
+# last two scale bytes reaches past the end of the scale buffer, and a load
+# that does so reads that whole dword as zero.  At k = 32, 160 and 2080 the
+# two bytes open the first dword of the last piece (which starts at byte 0,
+# 8 and 128 of the row's scales); at k = 96 and 224 they open its second
+# dword.  The last rows carry the check.
+@pytest.mark.parametrize("n,k", [(65540, 32), (65536, 160), (65544, 2080), (65536, 96),
+                                 (65539, 224)])
 def test_w4a16_gemv_wide_scale_row_end(n, k):
     wp, ws, s2 = synth.gemv_nvfp4_weight(n, k, "cpu", shape_id=11)
     x = synth.gemv_acts_bf16(8, k, "cpu", shape_id=11)
