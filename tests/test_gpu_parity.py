@@ -80,7 +80,11 @@ def test_quantize_bf16_nvfp4_bit_exact(rows, k, scale2):
     assert np.array_equal(host(p), op)
 
 
-@pytest.mark.parametrize("rows,k", [(1, 16), (7, 48), (40, 5120), (3, 20000), (9, 2064)])
+# k / 8 chunks of 16 bytes per row select the kernel: <= 256, 512, 768,
+# 1024, 2048 chunks per workgroup, or the long-row loop; each is run full
+# and ragged (k = 2064, 6160, 12304 leave part of the last chunk round empty).
+@pytest.mark.parametrize("rows,k", [(1, 16), (7, 48), (40, 5120), (3, 20000), (9, 2064),
+                                    (3, 8192), (2, 6160), (3, 16384), (2, 12304)])
 def test_quant_rowwise_fp8_bit_exact(rows, k):
     x = _with_edges(_bf16_rows((rows, k), 31 + rows, std=0.02))
     q, s = empty((rows, k), torch.uint8), empty((rows,), torch.float32)
@@ -91,11 +95,14 @@ def test_quant_rowwise_fp8_bit_exact(rows, k):
 
 
 @pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 5120), (1152, 1024),
-                                 (640, 8192), (256, 2176)])
+                                 (640, 8192), (256, 2176), (128, 8320), (128, 16384),
+                                 (128, 16512), (256, 24576)])
 def test_requant_blockfp8_rowwise_bit_exact(n, k):
     # k / 16 / 64 chunks per lane: 1 (partly and wholly used), 5, 8, and 3
     # with the third partly used; the row-pipelined kernel takes several rows
-    # per wave once n exceeds its resident waves.
+    # per wave once n exceeds its resident waves.  Longer rows take the
+    # workgroup-per-row kernel (k = 8320 just past the wave kernels, 16384 at
+    # its end) and the long-row loop (16512, 24576).
     cse = synth.fp8_block("cpu", m=1, n=n, k=k)
     w, grid = cse.w_block.clone(), cse.block_grid
     w[1, ::5] = 0x80                     # -0.0 codes
