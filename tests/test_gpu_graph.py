@@ -133,3 +133,36 @@ def test_captured_calls_replay_bit_exact():
         for i, ((_, outs), ref) in enumerate(zip(calls, eager)):
             for t, r in zip(outs, ref):
                 assert _same(t, r), f"replay {rep}: call {i} differs from its eager result"
+
+
+def test_cached_hit_replays_from_a_captured_graph():
+    """A cache hit enqueues no kernel and only makes the stream wait for the
+    derivation, so it may be captured (the miss, which allocates, ran
+    eagerly before): every replay equals the eager stateless projection."""
+    from tests.gpu_util import empty, filled
+    m, n, k = 130, 384, 640
+    cse = synth.fp8_block("cpu", m, n, k)
+    w, g, a = cse.w_block.to(DEV), cse.block_grid.to(DEV), cse.a_bf16.to(DEV)
+    aq, asc = empty((m, k), torch.uint8), empty((m,), torch.float32)
+    ref = filled((m, n), torch.bfloat16)
+    wr, wrs = empty((n, k), torch.uint8), empty((n,), torch.float32)
+    qp.fp8_rowwise_proj(qp.QP_FP8_BLOCK128, w, g, wr, wrs, a, aq, asc, ref)
+    c = qp.DerivedWeights()
+    try:
+        out = filled((m, n), torch.bfloat16)
+        aq2, asc2 = empty((m, k), torch.uint8), empty((m,), torch.float32)
+        c.fp8_rowwise_proj(qp.QP_FP8_BLOCK128, w, g, a, aq2, asc2, out)      # the miss
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            c.fp8_rowwise_proj(qp.QP_FP8_BLOCK128, w, g, a, aq2, asc2, out)  # a hit
+        for rep in range(3):
+            _scribble(out)
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            assert _same(out, ref), f"replay {rep}"
+        assert c.stats()[0] == 1
+    finally:
+        torch.cuda.synchronize()
+        c.close()
