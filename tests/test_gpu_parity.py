@@ -446,6 +446,45 @@ def test_cache_derives_once_and_matches_the_oracle():
         c.close()
 
 
+def test_cache_concurrent_requests_derive_once():
+    """Eight host threads ask for the same weight at once (ctypes releases
+    the GIL inside the call): the miss holds the cache's lock, so exactly
+    one derivation is launched and every thread gets the same buffers."""
+    import threading
+    m, n, k = 64, 256, 384
+    cse = synth.fp8_block("cpu", m, n, k)
+    w, g = dev(cse.w_block), dev(cse.block_grid)
+    c = qp.DerivedWeights()
+    try:
+        torch.cuda.synchronize()
+        before = qp.launch_count()
+        got, errs = [], []
+        go = threading.Barrier(8)
+
+        def ask():
+            try:
+                go.wait()
+                got.append(c.requant_w_blockfp8_rowwise(qp.QP_FP8_BLOCK128, w, g))
+            except Exception as e:          # reported below
+                errs.append(e)
+
+        ts = [threading.Thread(target=ask) for _ in range(8)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        assert not errs, errs
+        assert len(got) == 8 and len(set(got)) == 1
+        assert qp.launch_count() == before + 1
+        assert c.stats() == (1, n * k + 4 * n)
+        ow, ows = oracle.requant_w_blockfp8_rowwise(bits(cse.w_block), cse.block_grid.numpy())
+        wq = copy_from_address(got[0][0], (n, k), torch.uint8)
+        assert np.array_equal(host(wq), ow)
+    finally:
+        torch.cuda.synchronize()
+        c.close()
+
+
 def test_cached_projection_equals_stateless_across_streams():
     """Derive on a side stream, then use the hit on the current stream
     without synchronising the side stream: the hit orders the projection
