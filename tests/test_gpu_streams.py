@@ -1,8 +1,11 @@
 """Every entry point runs on the stream its caller passes (torch's current
 stream in the binding): calls on non-default streams, and independent calls
-on two streams at once, give the default-stream results bit for bit."""
+on two streams at once, give the default-stream results bit for bit; and no
+call waits for the GPU before it returns."""
 import pytest
 import torch
+
+import gemv_nvfp4_int8_amd as qp
 
 from tests.test_gpu_graph import _calls, _same, _scribble
 
@@ -51,3 +54,33 @@ def test_independent_gemvs_on_two_concurrent_streams():
         with torch.cuda.stream(s[i % 2]):
             fn()
     _check(calls, ref, "two streams")
+
+
+def test_calls_return_before_their_kernels_finish():
+    """No entry point synchronises the host: enqueueing twenty large GEMMs
+    (several milliseconds of GPU work) returns in a small part of that time,
+    and the results are those of one call."""
+    import time
+    m, n, k = 8192, 8192, 4096                  # ~0.2 ms per call
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(11)
+    a = torch.randint(0, 0x7E, (m, k), generator=g, device="cuda:0", dtype=torch.uint8)
+    w = torch.randint(0, 0x7E, (n, k), generator=g, device="cuda:0", dtype=torch.uint8)
+    sa = torch.rand(m, generator=g, device="cuda:0") + 0.5
+    sw = torch.rand(n, generator=g, device="cuda:0") + 0.5
+    ref = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty_like(ref)
+    qp.fp8_gemm_rowscale(a, sa, w, sw, ref)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        qp.fp8_gemm_rowscale(a, sa, w, sw, out)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    e1.record()
+    torch.cuda.synchronize()
+    gpu_ms = e0.elapsed_time(e1)
+    assert gpu_ms > 2.0, gpu_ms                 # the work really is long
+    assert host_ms < 0.5 * gpu_ms, (host_ms, gpu_ms)
+    assert _same(out, ref)
