@@ -133,3 +133,36 @@ def test_w4a16_gemv_wide_scale_row_end(n, k):
         qp.w4a16_gemv(dev(x[:m].contiguous()), dev(wp), dev(ws), s2, out)
         ref = oracle.w4a16_gemv(bits(x[:m]), wp.numpy(), ws.numpy(), s2)
         assert_gemv_close(host(out), ref, f"w4a16 {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (1, 33, 64), (3, 1, 32)])
+def test_int8_w4a8_prefill_single_rows_columns(m, n, k):
+    """The fused prefill (activation requant, then the int8 GEMM) at one row
+    or column and one scale block: its activation codes and scales bit-exact,
+    its output to the GEMM bound."""
+    a = _bf16((m, k), 741 + m)
+    w = _bf16((n, k), 742 + n, std=0.02)
+    ow, ows = oracle.requant_a_bf16_int8(bits(w))
+    aq, asc = empty((m, k), torch.int8), empty((m, k // 32), torch.float32)
+    out = filled((m, n), torch.bfloat16)
+    qp.int8_w4a8_prefill(dev(a), _t(ow), _t(ows), aq, asc, out)
+    oa, oas = oracle.requant_a_bf16_int8(bits(a))
+    assert np.array_equal(host(aq), oa)
+    assert np.array_equal(host(asc).view(np.uint32), oas.view(np.uint32))
+    assert_gemm_close(host(out), oracle.int8_gemm_blockscaled(oa, ow, oas, ows), f"prefill {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (3, 128, 256)])
+def test_fp8_rowwise_proj_single_row_one_block(m, n, k):
+    """The fused block-FP8 projection (weight requant, activation quant, GEMM)
+    at one activation row and a single 128 x 128 scale block or row of them."""
+    cse = synth.fp8_block("cpu", m=m, n=n, k=k)
+    wr, wrs = empty((n, k), torch.uint8), empty((n,), torch.float32)
+    aq, asc = empty((m, k), torch.uint8), empty((m,), torch.float32)
+    out = filled((m, n), torch.bfloat16)
+    qp.fp8_rowwise_proj(qp.QP_FP8_BLOCK128, dev(cse.w_block), dev(cse.block_grid), wr, wrs,
+                        dev(cse.a_bf16), aq, asc, out)
+    ow, ows = oracle.requant_w_blockfp8_rowwise(bits(cse.w_block), cse.block_grid.numpy())
+    oa, oas = oracle.quant_rowwise_fp8(bits(cse.a_bf16))
+    assert np.array_equal(host(wr), ow) and np.array_equal(host(aq), oa)
+    assert_gemm_close(host(out), oracle.fp8_gemm_rowscale(oa, oas, ow, ows), f"proj {m}x{n}x{k}")
