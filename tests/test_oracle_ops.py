@@ -73,6 +73,41 @@ def test_hw5_quant_rowwise_fp8():
     assert s[0] == _f32hex(c["expect_scale_hex"])
 
 
+def test_hw8_int8_divides_by_the_stored_scale():
+    """HW8: the int8 code of 0.28125 in a block of absmax 0.5625 is 63 when
+    the element is divided by the stored binary32 scale, and 64 under the
+    other reading (rounding the exact quotient 63.5).  The second assertion
+    recomputes that other reading with exact rationals, so the fixture
+    provably tells the two apart."""
+    c = _cases()["HW8"]
+    x = [float(t) for t in c["x"].split()]
+    q, s = oracle.requant_a_bf16_int8(_bf16(x)[None, :])
+    expect = np.array(c["expect_q"].split(), dtype=np.int8)
+    assert np.array_equal(q[0], expect)
+    assert s[0, 0] == _f32hex(c["expect_scale_hex"])
+    exact = Fraction(127) * Fraction(x[1]) / Fraction(max(abs(v) for v in x))
+    assert exact == Fraction(127, 2)                       # a midpoint
+    alt = round(exact)                                      # Python rounds ties to even
+    assert alt == int(c["exact_quotient_q1"]) != expect[1]
+
+
+def test_hw9_e4m3_row_divides_by_the_stored_scale():
+    """HW9: the E4M3 code of 1.453125 in a row of absmax 3.875 is 0x73 when
+    divided by the stored scale (quotient 168 + 2^-16), and 0x72 when the
+    exact quotient 168 (a midpoint of 160 and 176) is rounded instead."""
+    c = _cases()["HW9"]
+    x = [float(t) for t in c["x"].split()]
+    q, s = oracle.quant_rowwise_fp8(_bf16(x)[None, :])
+    expect = _hexbytes(c["expect_q"])
+    assert np.array_equal(q[0], expect)
+    assert s[0] == _f32hex(c["expect_scale_hex"])
+    exact = Fraction(448) * Fraction(x[1]) / Fraction(max(abs(v) for v in x))
+    assert exact == 168                                     # midpoint of 160 and 176
+    # torch's E4M3 cast rounds a binary32 to nearest-even; 168.0 is exact in it
+    alt = int(torch.tensor([float(exact)]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+    assert alt == int(c["exact_quotient_code1"], 16) != expect[1]
+
+
 def test_hw6_blockfp8_bf16_intermediate():
     c = _cases()["HW6"]
     code = int(c["code"], 16)
