@@ -1,8 +1,8 @@
 // cache.hip -- derived-weight cache: a weight is requantised on first use and
 // the result is kept for the life of the cache, keyed by the source weight's
 // device address (dispatch_proj_rowwise.rs, requant_weight_rowwise_fp8_cached
-// with its DerivedWeights cache; gemm_dense_int8.rs, requant_w_nvfp4_int8 as
-// a one-time conversion at load or lazily on first use).
+// with its DerivedWeights cache; gemm_dense_int8.rs, requant_w_nvfp4_int8,
+// whose int8 copy is made once per weight).
 //
 // Host code only.  The derivation itself is the stateless entry point's
 // kernel, enqueued on the caller's stream; the cache owns the derived device

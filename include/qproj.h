@@ -70,7 +70,8 @@ enum qp_weight_format {
  * Each value is dequantised as fl(e2m1 * e4m3 * scale2) (the first product is
  * exact), two sub-blocks are re-blocked into one 32-block, and the block is
  * quantised with s = amax/127, q = RNE(x/s).  Requires k % 32 == 0.
- * A one-time conversion per weight (at load or on first use).
+ * Each weight is derived once, either eagerly by the caller or by the
+ * derived-weight cache below on its first request.
  * ---------------------------------------------------------------------- */
 int requant_w_nvfp4_int8(const uint8_t *w_packed, const uint8_t *w_e4m3,
                          float scale2, int8_t *w_i8, float *w_scale,
@@ -282,8 +283,8 @@ int w4a16_gemv(const uint16_t *x, const uint8_t *w_packed, const uint8_t *w_e4m3
 /* ------------------------------------------------------------------------
  * Derived-weight cache (dispatch_proj_rowwise.rs,
  * requant_weight_rowwise_fp8_cached and its DerivedWeights cache, keyed by
- * the weight pointer; gemm_dense_int8.rs, requant_w_nvfp4_int8 as a
- * one-time conversion at load or lazily on first use).
+ * the weight pointer; gemm_dense_int8.rs, requant_w_nvfp4_int8, whose int8
+ * copy is made once per weight).
  *
  * A cache maps (derivation, source weight address) to a requantised copy
  * that the cache allocates with hipMalloc on the first request (a miss),
