@@ -29,6 +29,7 @@ QP_ERR_FORMAT = -4
 QP_ERR_HIP = -5
 QP_ERR_ALIGN = -6
 QP_ERR_ALLOC = -7
+QP_ERR_SCRATCH = -8
 
 QP_FP8_PER_ROW = 0
 QP_FP8_BLOCK128 = 1
@@ -67,6 +68,7 @@ def lib() -> ctypes.CDLL:
             "requant_a_bf16_int8": [P, P, P, U, U, P],
             "int8_gemm_blockscaled": [P, P, P, P, P, U, U, U, P],
             "int8_w4a8_prefill": [P, P, P, P, P, P, U, U, U, P],
+            "int8_w4a8_prefill_noalloc": [P, P, P, P, U, U, U, P],
             "int8_gemm_block_partials": [P, P, P, U, U, U, P],
             "quantize_bf16_nvfp4": [P, P, P, F, U, U, P],
             "w4a4_gemm": [P, P, P, P, P, F, F, U, U, U, P],
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.qproj_launch_count.argtypes = []
         L.qproj_status_string.restype = ctypes.c_char_p
         L.qproj_status_string.argtypes = [ctypes.c_int]
+        L.qproj_noalloc_scratch_bytes.restype = ctypes.c_uint64
+        L.qproj_noalloc_scratch_bytes.argtypes = []
         L.qproj_abi_version.restype = ctypes.c_int
         L.qproj_abi_version.argtypes = []
         _lib = L
@@ -208,6 +212,24 @@ def int8_w4a8_prefill(a_bf16, w_i8, w_scale, a_i8_scratch, a_scale_scratch,
     _check("int8_w4a8_prefill", lib().int8_w4a8_prefill(
         _ptr(a_bf16), _ptr(w_i8), _ptr(w_scale), _ptr(a_i8_scratch),
         _ptr(a_scale_scratch), _ptr(out), m, n, k, _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().qproj_noalloc_scratch_bytes())
+
+
+def int8_w4a8_prefill_noalloc(a_bf16, w_i8, w_scale, out, stream=None):
+    """int8_w4a8_prefill with the activation scratch held inside the library
+    (a fixed per-GPU array): allocates nothing; calls on one GPU must not
+    overlap."""
+    m, k = a_bf16.shape
+    n = w_i8.shape[0]
+    _need(a_bf16, "a_bf16", BF16, (m, k))
+    _need(w_i8, "w_i8", I8, (n, k))
+    _need(w_scale, "w_scale", F32, (n, k // 32))
+    _need(out, "out", BF16, (m, n))
+    _check("int8_w4a8_prefill_noalloc", lib().int8_w4a8_prefill_noalloc(
+        _ptr(a_bf16), _ptr(w_i8), _ptr(w_scale), _ptr(out), m, n, k, _stream(stream)))
 
 
 def int8_gemm_block_partials(a_i8, w_i8, p, stream=None):

@@ -57,6 +57,7 @@ const char *qproj_status_string(int status)
     case QP_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case QP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case QP_ERR_ALLOC: return "device memory for a derived weight could not be allocated";
+    case QP_ERR_SCRATCH: return "the problem needs more than the fixed scratch array of the no-allocation entry point";
     default: return "unknown status";
     }
 }

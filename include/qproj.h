@@ -48,6 +48,7 @@ extern "C" {
 #define QP_ERR_HIP (-5)    /* the HIP runtime rejected a launch             */
 #define QP_ERR_ALIGN (-6)  /* a pointer is not 16-byte aligned              */
 #define QP_ERR_ALLOC (-7)  /* a derived-weight cache could not allocate     */
+#define QP_ERR_SCRATCH (-8) /* the problem exceeds a fixed scratch array     */
 
 /* Weight format tags of an FP8 weight (dispatch_proj_rowwise.rs tests:
  * Fp8PerRow, Fp8BlockScaled, Fp8SingleScale, Bf16, Nvfp4). */
@@ -110,6 +111,24 @@ int int8_w4a8_prefill(const uint16_t *a_bf16, const int8_t *w_i8,
                       const float *w_scale, int8_t *a_i8_scratch,
                       float *a_scale_scratch, uint16_t *out,
                       uint32_t m, uint32_t n, uint32_t k, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as int8_w4a8_prefill, same kernels and bit-identical output, with the
+ * activation scratch held in a fixed device array inside the library
+ * (QP_NOALLOC_SCRATCH_BYTES per GPU, kept until the process ends) instead of
+ * caller buffers.  It allocates nothing.  The scratch needs
+ * align256(m*k) + 4*m*(k/32) bytes; a larger problem returns QP_ERR_SCRATCH
+ * and enqueues nothing.  All calls on one GPU share that GPU's array, so
+ * calls that overlap on one GPU (other streams, other threads) race: the
+ * caller must order them.  The first call on each device looks the array's
+ * address up once (hipGetSymbolAddress). */
+#define QP_NOALLOC_SCRATCH_BYTES (24u << 20)
+int int8_w4a8_prefill_noalloc(const uint16_t *a_bf16, const int8_t *w_i8,
+                              const float *w_scale, uint16_t *out,
+                              uint32_t m, uint32_t n, uint32_t k, void *stream);
+/* QP_NOALLOC_SCRATCH_BYTES, as built into the library. */
+uint64_t qproj_noalloc_scratch_bytes(void);
 
 /* Test export: the exact int32 partial sum of every 32-K block,
  * p [m, n, k/32] (p[(i*n + j)*(k/32) + b] = P_b[i,j]), computed by the same

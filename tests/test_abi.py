@@ -232,6 +232,8 @@ _EXTENT_CALLS = {
         FAKE, FAKE2, FAKE, FAKE2, FAKE, m, n, k, None), (4, 256, 256)),
     "int8_w4a8_prefill": (lambda m, n, k: L.int8_w4a8_prefill(
         FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
+    "int8_w4a8_prefill_noalloc": (lambda m, n, k: L.int8_w4a8_prefill_noalloc(
+        FAKE, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
     "int8_gemm_block_partials": (lambda m, n, k: L.int8_gemm_block_partials(
         FAKE, FAKE2, FAKE, m, n, k, None), (4, 256, 256)),
     "quantize_bf16_nvfp4": (lambda r, k: L.quantize_bf16_nvfp4(
@@ -327,6 +329,8 @@ _PTR_CALLS = {
         p[0], p[1], p[2], p[3], p[4], 4, 256, 256, None), 5),
     "int8_w4a8_prefill": (lambda p: L.int8_w4a8_prefill(
         p[0], p[1], p[2], p[3], p[4], p[5], 4, 256, 256, None), 6),
+    "int8_w4a8_prefill_noalloc": (lambda p: L.int8_w4a8_prefill_noalloc(
+        p[0], p[1], p[2], p[3], 4, 256, 256, None), 4),
     "int8_gemm_block_partials": (lambda p: L.int8_gemm_block_partials(
         p[0], p[1], p[2], 4, 256, 256, None), 3),
     "quantize_bf16_nvfp4": (lambda p: L.quantize_bf16_nvfp4(p[0], p[1], p[2], 1.0, 4, 256, None), 3),
@@ -363,3 +367,24 @@ def test_every_pointer_is_checked_before_any_launch(name):
             st = call(p)
             assert st == want, (name, i, bad, st)
             assert qp.launch_count() == before
+
+
+def test_noalloc_prefill_refuses_problems_beyond_its_scratch_array():
+    """The no-allocation prefill keeps its activation scratch (int8 codes,
+    then 256-byte aligned F32 scales) in a fixed array; a problem that needs
+    more is refused on the host with QP_ERR_SCRATCH, launching nothing."""
+    cap = qp.noalloc_scratch_bytes()
+    assert cap == 24 << 20
+
+    def need(m, k):
+        return (m * k + 255) // 256 * 256 + 4 * m * (k // 32)
+
+    k = 5120
+    m_fit = max(m for m in range(1, 8192) if need(m, k) <= cap)
+    before = qp.launch_count()
+    assert L.int8_w4a8_prefill_noalloc(FAKE, FAKE2, FAKE, FAKE2, m_fit + 1, 128, k, None) \
+        == qp.QP_ERR_SCRATCH
+    assert L.int8_w4a8_prefill_noalloc(FAKE, FAKE2, FAKE, FAKE2, 1, 1, 32 * 800000, None) \
+        == qp.QP_ERR_SCRATCH
+    assert qp.launch_count() == before
+    assert qp.status_string(qp.QP_ERR_SCRATCH) != "unknown status"
