@@ -156,11 +156,12 @@ __device__ __forceinline__ void div_all(const ScaleDiv &d, const float *x, float
     }
 }
 
-// Hardware converters.  Each was compared on this part with the software
-// encoders above over every binary32 input of its domain (both signs) and
-// agrees bit for bit: E4M3 for |y| <= 448 (beyond 464 the converter returns
-// NaN, so inputs are clamped to +-448 first, which RNE maps to 448 anyway),
-// E2M1 for |y| <= 8 (inputs are clamped to +-6), BF16 for every finite y.
+// Hardware converters.  Through the quantizer kernels they are checked bit
+// for bit against the oracle's grid-search encoders on every BF16 input of
+// their domain at unit scale (every grid point, midpoint and neighbour, both
+// signs): E4M3 for |y| <= 448 (beyond 464 the converter returns NaN, so
+// inputs are clamped to +-448 first, which RNE maps to 448 anyway), E2M1 for
+// |y| <= 6 (inputs are clamped to +-6), int8 for |y| <= 127.
 __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b)
 {
     a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
