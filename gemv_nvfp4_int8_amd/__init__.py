@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "int8_gemm_blockscaled": [P, P, P, P, P, U, U, U, P],
             "int8_w4a8_prefill": [P, P, P, P, P, P, U, U, U, P],
             "int8_w4a8_prefill_noalloc": [P, P, P, P, U, U, U, P],
+            "qproj_encode_test": [I, P, P, U, P],
             "int8_gemm_block_partials": [P, P, P, U, U, U, P],
             "quantize_bf16_nvfp4": [P, P, P, F, U, U, P],
             "w4a4_gemm": [P, P, P, P, P, F, F, U, U, U, P],
@@ -212,6 +213,20 @@ def int8_w4a8_prefill(a_bf16, w_i8, w_scale, a_i8_scratch, a_scale_scratch,
     _check("int8_w4a8_prefill", lib().int8_w4a8_prefill(
         _ptr(a_bf16), _ptr(w_i8), _ptr(w_scale), _ptr(a_i8_scratch),
         _ptr(a_scale_scratch), _ptr(out), m, n, k, _stream(stream)))
+
+
+QP_ENC_E4M3_NOSAT, QP_ENC_E2M1_NOSAT, QP_ENC_INT8 = 0, 1, 2
+QP_ENC_E4M3, QP_ENC_E2M1, QP_ENC_E4M3_SCALE = 3, 4, 5
+
+
+def encode_test(kind, y, out, stream=None):
+    """Test export: the kernels' device encoder `kind` on float32 values y
+    (a 1-D tensor, length a multiple of 8), one code byte per value in out."""
+    n = y.numel()
+    _need(y, "y", F32, (n,))
+    _need(out, "out", U8, (n,))
+    _check("qproj_encode_test", lib().qproj_encode_test(int(kind), _ptr(y), _ptr(out), n,
+                                                        _stream(stream)))
 
 
 def noalloc_scratch_bytes() -> int:

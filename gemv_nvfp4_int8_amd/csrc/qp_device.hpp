@@ -106,15 +106,49 @@ __device__ __forceinline__ int enc_i8(float y)
 // correctly rounded f32 division).
 __device__ __forceinline__ float div_rn(float x, float y) { return x / y; }
 
-// Correctly rounded x / s for many x and one s, in three operations per x.
-// With r = RN(1/s) (one IEEE division per scale), q0 = RN(x*r) is within an
-// ulp of x/s, the remainder x - q0*s is exact in one FMA, and
-// RN(q0 + rem*r) is RN(x/s) (Markstein's correction theorem: a reciprocal
-// within half an ulp and a quotient within one ulp give the correctly
-// rounded quotient, barring underflow and overflow).  The correction loses
-// the sign of a zero quotient (-0/s would come out +0), and RN(x/s) always
-// has the sign of q0, so q0's sign bit is copied onto the result.  Scales
-// outside [2^-100, 2^100] fall back to the division instruction sequence.
+// One correction step of a quotient by a known reciprocal (Markstein): with
+// r = RN(1/s) and q0 = RN(x*r) (within an ulp of x/s), the remainder
+// x - q0*s is exact in one FMA, and RN(q0 + rem*r) is RN(x/s), barring
+// underflow and overflow in the intermediate steps.  The remainder is formed
+// negated, t = q0*s - x, and enters the second FMA with its sign flipped:
+// that is the same value whenever it is nonzero, while an exactly zero
+// remainder becomes -0, so q0 + (-0)*r keeps q0's sign and x = -0 gives
+// -0 (the plain form would turn it into +0).
+__device__ __forceinline__ float div_corr(float x, float s, float r)
+{
+    const float q0 = x * r;
+    const float t = __builtin_fmaf(q0, s, -x);
+    return __builtin_fmaf(-t, r, q0);
+}
+
+// fl(a / 127) and fl(a / 448) through div_corr with the constant's correctly
+// rounded reciprocal.  Valid for a == 0 and for a in [2^-100, 2^126], where no
+// step under- or overflows; there the result depends on a's significand
+// alone (scaling a by a power of two scales every step exactly), and it was
+// checked against the IEEE quotient for every binary32 significand.
+constexpr float RCP_127 = 0x1.020408p-7f;   // RN(1/127)
+constexpr float RCP_448 = 0x1.24924ap-9f;   // RN(1/448)
+__device__ __forceinline__ bool const_div_ok(float a)
+{
+    return a == 0.0f || (a >= 0x1p-100f && a <= 0x1p126f);
+}
+
+// a / 127 (or 448) correctly rounded, for one value per lane: the reciprocal
+// form when every active lane of the wave allows it, else the division
+// instruction sequence.
+template <int B>
+__device__ __forceinline__ float div_by_const(float a)
+{
+    constexpr float R = B == 127 ? RCP_127 : RCP_448;
+    static_assert(B == 127 || B == 448, "constant divisors: 127, 448");
+    if (__all(const_div_ok(a)))
+        return div_corr(a, (float)B, R);
+    return div_rn(a, (float)B);
+}
+
+// Correctly rounded x / s for many x and one s, in three operations per x:
+// r = RN(1/s) (one IEEE division per scale), then div_corr.  Scales outside
+// [2^-100, 2^100] take the division instruction sequence instead.
 struct ScaleDiv {
     float s, r;
     bool fast;
@@ -123,15 +157,12 @@ struct ScaleDiv {
         fast = s_ >= 0x1p-100f && s_ <= 0x1p100f;
         r = fast ? div_rn(1.0f, s_) : 0.0f;
     }
-    // The FMA-corrected quotient alone (valid when `fast`), without a branch.
-    __device__ __forceinline__ float quick(float x) const
+    // From a reciprocal known to be RN(1/s_) (a table entry).
+    __device__ __forceinline__ ScaleDiv(float s_, float r_) : s(s_), r(r_)
     {
-        float q0 = x * r;
-        float rem = __builtin_fmaf(-q0, s, x);
-        float q = __builtin_fmaf(rem, r, q0);
-        return __uint_as_float((__float_as_uint(q) & 0x7FFFFFFFu) |
-                               (__float_as_uint(q0) & 0x80000000u));
+        fast = s_ >= 0x1p-100f && s_ <= 0x1p100f;
     }
+    __device__ __forceinline__ float quick(float x) const { return div_corr(x, s, r); }
     __device__ __forceinline__ float operator()(float x) const
     {
         return fast ? quick(x) : div_rn(x, s);
@@ -157,11 +188,14 @@ __device__ __forceinline__ void div_all(const ScaleDiv &d, const float *x, float
 }
 
 // Hardware converters.  Through the quantizer kernels they are checked bit
-// for bit against the oracle's grid-search encoders on every BF16 input of
+// for bit against grid-search reference encoders on every BF16 input of
 // their domain at unit scale (every grid point, midpoint and neighbour, both
-// signs): E4M3 for |y| <= 448 (beyond 464 the converter returns NaN, so
-// inputs are clamped to +-448 first, which RNE maps to 448 anyway), E2M1 for
-// |y| <= 6 (inputs are clamped to +-6), int8 for |y| <= 127.
+// signs), and directly, through the encoder test export, on every binary32
+// value within 64 ulps of each rounding boundary and on a strided sample of
+// the rest of the domain.  E4M3 for |y| < 464 (from 464 on the converter
+// returns the NaN code, so callers whose values may reach it clamp them to
+// +-448 first, which RNE maps to 448 anyway), E2M1 for |y| <= 8, int8 for
+// |y| <= 127.5.
 __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b)
 {
     a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
@@ -177,40 +211,64 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Four E4M3 codes of (a, b, c, d) in one dword, a in the low byte.
-__device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d)
+// Four E4M3 codes of (a, b, c, d) in one dword, a in the low byte, for
+// values known to satisfy |y| < 464 (no clamp).
+__device__ __forceinline__ uint32_t cvt_e4m3x4_nosat(float a, float b, float c, float d)
 {
-    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// Eight E2M1 codes of v[0..7] in one dword, v[0] in the low nibble.
-__device__ __forceinline__ uint32_t cvt_e2m1x8(const float *v)
+// The same for any finite values: saturated to +-448 first.
+__device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float d)
 {
-    float c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        c[i] = __builtin_amdgcn_fmed3f(v[i], -6.0f, 6.0f);
+    return cvt_e4m3x4_nosat(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                            __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f),
+                            __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f),
+                            __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f));
+}
+
+// E4M3 code of a block scale t >= 0 (finite), saturated at 448.
+__device__ __forceinline__ uint32_t enc_e4m3_scale(float t)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(t, 448.0f), 0.0f, 0,
+                                                     false) & 0xFFu;
+}
+
+// Eight E2M1 codes of v[0..7] in one dword, v[0] in the low nibble, for
+// values known to satisfy |y| <= 8 (no clamp).
+__device__ __forceinline__ uint32_t cvt_e2m1x8_nosat(const float *c)
+{
     uint32_t o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, c[0], c[1], 1.0f, 0);
     o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, c[2], c[3], 1.0f, 1);
     o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, c[4], c[5], 1.0f, 2);
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, c[6], c[7], 1.0f, 3);
 }
 
-// Four int8 codes RNE(v[i]) for |v| < 127.5, v[0] in the low byte: rounded
-// to an integer, biased by 128 (exact) and packed by the u8 converter, then
-// un-biased with one XOR.
-__device__ __forceinline__ uint32_t cvt_i8x4(const float *v)
+// The same for any finite values: saturated to +-6 first.
+__device__ __forceinline__ uint32_t cvt_e2m1x8(const float *v)
 {
-    uint32_t o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[0]) + 128.0f, 0, 0u);
-    o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[1]) + 128.0f, 1, o);
-    o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[2]) + 128.0f, 2, o);
-    o = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(v[3]) + 128.0f, 3, o);
-    return o ^ 0x80808080u;
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        c[i] = __builtin_amdgcn_fmed3f(v[i], -6.0f, 6.0f);
+    return cvt_e2m1x8_nosat(c);
+}
+
+// Four int8 codes RNE(v[i]) for |v| < 127.5, v[0] in the low byte.  Adding
+// 1.5 * 2^23 rounds v to an integer (the sum lies in [2^23, 2^24), where the
+// binary32 spacing is 1, so the addition's own round-to-nearest-even is the
+// integer rounding) and leaves that integer, two's complement, in the low
+// byte of the sum's bit pattern; v_perm gathers the four low bytes.
+__device__ __forceinline__ uint32_t pack_i8x4(const float *v)
+{
+    const uint32_t b0 = __float_as_uint(v[0] + 12582912.0f);
+    const uint32_t b1 = __float_as_uint(v[1] + 12582912.0f);
+    const uint32_t b2 = __float_as_uint(v[2] + 12582912.0f);
+    const uint32_t b3 = __float_as_uint(v[3] + 12582912.0f);
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);   // b0.0, b1.0, 0, 0
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);   // 0, 0, b2.0, b3.0
+    return lo | hi;
 }
 
 // The two E2M1 values of byte SEL of w (low nibble first), exactly.
@@ -218,6 +276,13 @@ template <int SEL>
 __device__ __forceinline__ f32x2 e2m1_pair(uint32_t w)
 {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// The two E2M1 values of byte SEL of w (low nibble first) in FP16, exactly.
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1_pair_f16(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
 }
 
 // ------------------------------------------------------- wave reductions

@@ -1,7 +1,9 @@
 // quant.hip -- streaming quantizers and weight requantizers for gfx950.
 //
 // All of them are HBM-bound: every byte is read once with 16-byte vector
-// loads, codes are written with 8- or 16-byte stores, and absmax reductions
+// loads, codes are written with 8- or 16-byte non-temporal stores (about 3-6%
+// faster than plain stores here: the outputs are not read back by the same
+// kernel), and absmax reductions
 // stay in registers (per-block kernels) or use wave shuffles plus one LDS
 // exchange per workgroup (per-row kernels).
 #include <type_traits>
@@ -58,17 +60,17 @@ __global__ __launch_bounds__(256) void k_requant_a_bf16_int8(
             amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
         amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, WAVE));
         amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, WAVE));
-        const float sc = div_rn(amax, 127.0f);
+        const float sc = div_by_const<127>(amax);
         u32x2 out = {0, 0};
         if (sc != 0.0f) {
             ScaleDiv d(sc);
             float t[8];
             div_all<8>(d, x, t);
-            out[0] = cvt_i8x4(&t[0]);
-            out[1] = cvt_i8x4(&t[4]);
+            out[0] = pack_i8x4(&t[0]);
+            out[1] = pack_i8x4(&t[4]);
         }
         if (c < nchunks) {
-            *reinterpret_cast<u32x2 *>(q + (size_t)c * 8) = out;
+            __builtin_nontemporal_store(out, reinterpret_cast<u32x2 *>(q + (size_t)c * 8));
             if ((c & 3u) == 0u)
                 s[c >> 2] = sc;
         }
@@ -116,17 +118,20 @@ __global__ __launch_bounds__(256) void k_requant_w_nvfp4_int8(
 #pragma unroll
     for (int u = 0; u < QR; ++u) {
         const uint32_t h = base + 256u * u;     // nhalves is even: a block's lanes agree
-        const float dd = dec_e4m3(scb[u]);
+        // e2m1 * e4m3 is exact in FP16 (at most 6 significant bits, magnitudes
+        // 2^-10 .. 2688), so it is formed two at a time in packed FP16; the
+        // one rounded step, times scale2, is a mixed-precision FMA.
+        const _Float16 dh = (_Float16)dec_e4m3(scb[u]);
+        const f16x2 dd2 = (f16x2){dh, dh};
         float v[16];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-            // E2M1 pairs of the four bytes of word w (low nibble = even element)
-            f32x2 e[4] = {e2m1_pair<0>(p[u][w]), e2m1_pair<1>(p[u][w]), e2m1_pair<2>(p[u][w]),
-                          e2m1_pair<3>(p[u][w])};
+            const f16x2 e[4] = {e2m1_pair_f16<0>(p[u][w]) * dd2, e2m1_pair_f16<1>(p[u][w]) * dd2,
+                                e2m1_pair_f16<2>(p[u][w]) * dd2, e2m1_pair_f16<3>(p[u][w]) * dd2};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v[8 * w + 2 * j] = (e[j][0] * dd) * scale2;      // e2m1*e4m3 is exact
-                v[8 * w + 2 * j + 1] = (e[j][1] * dd) * scale2;
+                v[8 * w + 2 * j] = (float)e[j][0] * scale2;
+                v[8 * w + 2 * j + 1] = (float)e[j][1] * scale2;
             }
         }
         float amax = 0.0f;
@@ -134,17 +139,17 @@ __global__ __launch_bounds__(256) void k_requant_w_nvfp4_int8(
         for (int i = 0; i < 16; ++i)
             amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
         amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, WAVE));
-        const float sc = div_rn(amax, 127.0f);
+        const float sc = div_by_const<127>(amax);
         u32x4 o = {0, 0, 0, 0};
         if (sc != 0.0f) {
             ScaleDiv d(sc);
             div_all<16>(d, v, v);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                o[j] = cvt_i8x4(&v[4 * j]);
+                o[j] = pack_i8x4(&v[4 * j]);
         }
         if (h < nhalves) {
-            *reinterpret_cast<u32x4 *>(q + (size_t)h * 16) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(q + (size_t)h * 16));
             if ((h & 1u) == 0u)
                 s[h >> 1] = sc;
         }
@@ -170,12 +175,27 @@ hipError_t launch_requant_w_nvfp4_int8(const uint8_t *packed, const uint8_t *sc1
 // fl(6*scale2))), d = fl(e4m3(sb)*scale2), code = E2M1(fl(x/d)), or +0
 // everywhere when d == 0.  The block scales of four blocks (8 lanes) are
 // gathered into one dword store.
+//
+// The divisions are the kernel's arithmetic bound, so none is repeated per
+// block: fl(amax / fl(6*scale2)) is one correction step with that divisor's
+// reciprocal (one IEEE division per thread), and the decoded scale d takes
+// only 127 values per call, whose reciprocals a workgroup computes once into
+// LDS.  With a normal block scale that did not saturate, every |x/d| stays
+// below 6 * (1 + 2^-4) < 8, inside the E2M1 converter's checked range, so
+// the clamp to +-6 is skipped when a whole wave is in that case.
 // ---------------------------------------------------------------------------
 template <int QR>
 __global__ __launch_bounds__(256) void k_quantize_bf16_nvfp4(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ packed,
     uint8_t *__restrict__ sc16, float scale2, uint32_t nchunks)
 {
+    // RN(1/d) for d = fl(e4m3(c)*scale2), c = 0..126; 0 marks a d outside
+    // the range where the correction step is valid (ScaleDiv::fast).
+    __shared__ float rtab[128];
+    if (threadIdx.x < 128) {
+        const float d = dec_e4m3(threadIdx.x & 0x7Fu) * scale2;
+        rtab[threadIdx.x] = (d >= 0x1p-100f && d <= 0x1p100f) ? div_rn(1.0f, d) : 0.0f;
+    }
     const uint32_t base = blockIdx.x * (256u * QR) + threadIdx.x;
     const int lane = threadIdx.x & 63;
     u32x4 raw[QR];
@@ -187,6 +207,9 @@ __global__ __launch_bounds__(256) void k_quantize_bf16_nvfp4(
             raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + (size_t)c * 8));
     }
     const float six_s2 = 6.0f * scale2;
+    const bool six_ok = six_s2 >= 0x1p-60f && six_s2 <= 0x1p60f;
+    const float r6 = six_ok ? div_rn(1.0f, six_s2) : 0.0f;
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < QR; ++u) {
         const uint32_t c = base + 256u * u;     // nchunks % 4 == 0: a block's lanes agree
@@ -201,19 +224,26 @@ __global__ __launch_bounds__(256) void k_quantize_bf16_nvfp4(
         for (int i = 0; i < 8; ++i)
             amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
         amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, WAVE));
-        const uint32_t sb = enc_e4m3(div_rn(amax, six_s2));
+        float t;
+        if (__all(six_ok && (amax == 0.0f || (amax >= 0x1p-60f && amax <= 0x1p60f))))
+            t = div_corr(amax, six_s2, r6);
+        else
+            t = div_rn(amax, six_s2);
+        // E4M3 of t >= 0 (saturated at 448) by the converter
+        const uint32_t sb = enc_e4m3_scale(t);
         const float d = dec_e4m3(sb) * scale2;
         uint32_t codes = 0;
         if (d != 0.0f) {
-            ScaleDiv dv(d);
-            div_all<8>(dv, v, v);
-            codes = cvt_e2m1x8(v);
+            const ScaleDiv dv(d, rtab[sb]);
+            float q[8];
+            div_all<8>(dv, v, q);
+            codes = __all(sb >= 0x08u && t < 448.0f) ? cvt_e2m1x8_nosat(q) : cvt_e2m1x8(q);
         }
         // scales of the blocks of lanes 8g .. 8g+7 (every other lane) -> lane 8g
         const uint32_t w4 = sb | (__shfl_down(sb, 2, WAVE) << 8) |
                             (__shfl_down(sb, 4, WAVE) << 16) | (__shfl_down(sb, 6, WAVE) << 24);
         if (c < nchunks) {
-            *reinterpret_cast<uint32_t *>(packed + (size_t)c * 4) = codes;
+            __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(packed + (size_t)c * 4));
             if ((lane & 7) == 0) {
                 // c % 8 == 0, so block c/2 starts a 4-byte-aligned word
                 if (c + 8 <= nchunks)
@@ -238,8 +268,18 @@ hipError_t launch_quantize_bf16_nvfp4(const uint16_t *x, uint8_t *packed,
 }
 
 // ---------------------------------------------------------------------------
-// Per-row kernels: one 256-thread workgroup per row (the block-scaled FP8
-// requant below also has a one-wave-per-row form).
+// Per-row kernels.  A row of up to 64*CPL 16-byte chunks is one wave's (four
+// rows per workgroup): the chunks stay in registers between the absmax pass
+// and the encode pass, so every input byte is read once; lane l takes
+// chunks l, l + 64, ..., so every load and store instruction covers one
+// contiguous window; the row absmax is a wave reduction alone (no LDS, no
+// barrier); and the scale, one per row, is wave-uniform, so its division
+// path is chosen once.  Longer rows take a workgroup per row and two passes
+// over global memory.
+//
+// The row scale s = fl(amax/448) bounds every quotient: |x/s| <= amax/s <=
+// 448 * (1 + 2^-23), so its RNE binary32 value is at most 448 plus one ulp,
+// below 464, where the E4M3 converter rounds to 448 by itself: no clamp.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float block_max_256(float v, float *red)
 {
@@ -252,10 +292,8 @@ __device__ __forceinline__ float block_max_256(float v, float *red)
                            __builtin_fmaxf(red[2], red[3]));
 }
 
-// E4M3 codes of v[0..7] / sc (correctly rounded quotients) in two dwords;
-// all +0 when the scale is 0.
-// E4M3 codes of v[0..7] / d.s for a scale whose `fast` flag is known to be
-// FAST (callers branch once per scale, not once per element).
+// E4M3 codes of v[0..7] / d.s in two dwords (quotients below 464 in
+// magnitude), by the path FAST (the caller branches once per scale).
 template <bool FAST>
 __device__ __forceinline__ u32x2 enc8_e4m3_path(const float *v, const ScaleDiv &d)
 {
@@ -263,38 +301,85 @@ __device__ __forceinline__ u32x2 enc8_e4m3_path(const float *v, const ScaleDiv &
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         t[i] = FAST ? d.quick(v[i]) : div_rn(v[i], d.s);
-    return (u32x2){cvt_e4m3x4(t[0], t[1], t[2], t[3]), cvt_e4m3x4(t[4], t[5], t[6], t[7])};
+    return (u32x2){cvt_e4m3x4_nosat(t[0], t[1], t[2], t[3]),
+                   cvt_e4m3x4_nosat(t[4], t[5], t[6], t[7])};
 }
 
-__device__ __forceinline__ u32x2 enc8_e4m3(const float *v, const ScaleDiv &d, bool zero)
+// Row-wise FP8 quantizer (dispatch_proj_rowwise.rs, quant_rowwise_fp8):
+// s = fl(amax/448), code = E4M3(fl(x/s)), or scale 0 and +0 codes.
+template <int CPL>
+__global__ __launch_bounds__(256) void k_quant_rowwise_fp8_wave(
+    const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
+    float *__restrict__ s, uint32_t rows, uint32_t k)
 {
-    u32x2 o = {0, 0};
-    if (!zero) {
-        float t[8];
-        div_all<8>(d, v, t);
-        o[0] = cvt_e4m3x4(t[0], t[1], t[2], t[3]);
-        o[1] = cvt_e4m3x4(t[4], t[5], t[6], t[7]);
+    const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows)
+        return;                          // the whole wave
+    const uint16_t *xr = x + (size_t)row * k;
+    uint8_t *qr = q + (size_t)row * k;
+    const uint32_t nch = k / 8;
+    u32x4 raw[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t c = lane + 64u * j;
+        raw[j] = (u32x4){0, 0, 0, 0};
+        if (c < nch)
+            raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)c * 8));
     }
-    return o;
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16_lo(raw[j][i])),
+                                                         __builtin_fabsf(bf16_hi(raw[j][i]))));
+    amax = wave_max(amax);
+    const float sc = div_by_const<448>(amax);
+    const ScaleDiv dv(sc);
+    auto encode = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const uint32_t c = lane + 64u * j;
+            if (c < nch) {
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = bf16_lo(raw[j][i]);
+                    v[2 * i + 1] = bf16_hi(raw[j][i]);
+                }
+                __builtin_nontemporal_store(
+                    sc != 0.0f ? enc8_e4m3_path<FAST>(v, dv) : (u32x2){0, 0},
+                    reinterpret_cast<u32x2 *>(qr + (size_t)c * 8));
+            }
+        }
+    };
+    if (dv.fast)
+        encode(std::true_type{});
+    else
+        encode(std::false_type{});
+    if (lane == 0)
+        s[row] = sc;
 }
 
-// Row-wise FP8 quantizer (dispatch_proj_rowwise.rs, quant_rowwise_fp8).
-// CPT 16-byte chunks (8 BF16 each) per thread stay in registers between the
-// absmax pass and the encode pass, so each input byte is read once.
+// Rows longer than a wave's registers hold: a workgroup per row, CPT chunks
+// per thread in registers (one pass over global memory).
 template <int CPT>
-__global__ __launch_bounds__(256) void k_quant_rowwise_fp8(
+__global__ __launch_bounds__(256) void k_quant_rowwise_fp8_wg(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
     float *__restrict__ s, uint32_t k)
 {
     __shared__ float red[4];
     const uint32_t row = blockIdx.x;
     const uint16_t *xr = x + (size_t)row * k;
+    uint8_t *qr = q + (size_t)row * k;
     const uint32_t nch = k / 8;
     u32x4 raw[CPT];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        uint32_t c = threadIdx.x + 256u * j;
+        const uint32_t c = threadIdx.x + 256u * j;
         raw[j] = (u32x4){0, 0, 0, 0};
         if (c < nch)
             raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)c * 8));
@@ -304,26 +389,36 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8(
                                                          __builtin_fabsf(bf16_hi(raw[j][i]))));
     }
     amax = block_max_256(amax, red);
-    const float sc = div_rn(amax, 448.0f);
+    const float sc = div_by_const<448>(amax);
     const ScaleDiv dv(sc);
+    auto encode = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        uint32_t c = threadIdx.x + 256u * j;
-        if (c < nch) {
-            float v[8];
+        for (int j = 0; j < CPT; ++j) {
+            const uint32_t c = threadIdx.x + 256u * j;
+            if (c < nch) {
+                float v[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = bf16_lo(raw[j][i]);
-                v[2 * i + 1] = bf16_hi(raw[j][i]);
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = bf16_lo(raw[j][i]);
+                    v[2 * i + 1] = bf16_hi(raw[j][i]);
+                }
+                __builtin_nontemporal_store(
+                    sc != 0.0f ? enc8_e4m3_path<FAST>(v, dv) : (u32x2){0, 0},
+                    reinterpret_cast<u32x2 *>(qr + (size_t)c * 8));
             }
-            *reinterpret_cast<u32x2 *>(q + (size_t)row * k + (size_t)c * 8) = enc8_e4m3(v, dv, sc == 0.0f);
         }
-    }
+    };
+    if (dv.fast)
+        encode(std::true_type{});
+    else
+        encode(std::false_type{});
     if (threadIdx.x == 0)
         s[row] = sc;
 }
 
-// Long rows: the same arithmetic in two passes over global memory.
+// Long rows: the same arithmetic, a workgroup per row, in two passes over
+// global memory.
 __global__ __launch_bounds__(256) void k_quant_rowwise_fp8_long(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
     float *__restrict__ s, uint32_t k)
@@ -341,7 +436,7 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8_long(
                                                          __builtin_fabsf(bf16_hi(r[i]))));
     }
     amax = block_max_256(amax, red);
-    const float sc = div_rn(amax, 448.0f);
+    const float sc = div_by_const<448>(amax);
     const ScaleDiv dv(sc);
     for (uint32_t c = threadIdx.x; c < nch; c += 256) {
         u32x4 r = *reinterpret_cast<const u32x4 *>(xr + (size_t)c * 8);
@@ -351,7 +446,10 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8_long(
             v[2 * i] = bf16_lo(r[i]);
             v[2 * i + 1] = bf16_hi(r[i]);
         }
-        *reinterpret_cast<u32x2 *>(q + (size_t)row * k + (size_t)c * 8) = enc8_e4m3(v, dv, sc == 0.0f);
+        u32x2 o = {0, 0};
+        if (sc != 0.0f)
+            o = dv.fast ? enc8_e4m3_path<true>(v, dv) : enc8_e4m3_path<false>(v, dv);
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(q + (size_t)row * k + (size_t)c * 8));
     }
     if (threadIdx.x == 0)
         s[row] = sc;
@@ -360,20 +458,20 @@ __global__ __launch_bounds__(256) void k_quant_rowwise_fp8_long(
 hipError_t launch_quant_rowwise_fp8(const uint16_t *x, uint8_t *q, float *s,
                                     uint32_t rows, uint32_t k, hipStream_t st)
 {
-    uint32_t nch = k / 8;
-    dim3 g(rows), b(256);
-    if (nch <= 256)
-        hipLaunchKernelGGL(k_quant_rowwise_fp8<1>, g, b, 0, st, x, q, s, k);
-    else if (nch <= 512)
-        hipLaunchKernelGGL(k_quant_rowwise_fp8<2>, g, b, 0, st, x, q, s, k);
-    else if (nch <= 768)
-        hipLaunchKernelGGL(k_quant_rowwise_fp8<3>, g, b, 0, st, x, q, s, k);
-    else if (nch <= 1024)
-        hipLaunchKernelGGL(k_quant_rowwise_fp8<4>, g, b, 0, st, x, q, s, k);
-    else if (nch <= 2048)
-        hipLaunchKernelGGL(k_quant_rowwise_fp8<8>, g, b, 0, st, x, q, s, k);
+    const uint32_t nch = k / 8;
+    const dim3 gw((rows + 3) / 4), b(256);
+#define QP_ROW_WAVE(C)                                                                        \
+    else if (nch <= 64u * C) hipLaunchKernelGGL(k_quant_rowwise_fp8_wave<C>, gw, b, 0, st, x, q, \
+                                                 s, rows, k);
+    if (false) {
+    }
+    QP_ROW_WAVE(1) QP_ROW_WAVE(2) QP_ROW_WAVE(4) QP_ROW_WAVE(6) QP_ROW_WAVE(8)
+    QP_ROW_WAVE(10) QP_ROW_WAVE(12) QP_ROW_WAVE(16)
+    else if (nch <= 256u * 8)
+        hipLaunchKernelGGL(k_quant_rowwise_fp8_wg<8>, dim3(rows), b, 0, st, x, q, s, k);
     else
-        hipLaunchKernelGGL(k_quant_rowwise_fp8_long, g, b, 0, st, x, q, s, k);
+        hipLaunchKernelGGL(k_quant_rowwise_fp8_long, dim3(rows), b, 0, st, x, q, s, k);
+#undef QP_ROW_WAVE
     count_launch();
     return hipGetLastError();
 }
@@ -382,69 +480,32 @@ hipError_t launch_quant_rowwise_fp8(const uint16_t *x, uint8_t *q, float *s,
 // Block-scaled FP8 -> row-wise FP8 (dispatch_proj_rowwise.rs,
 // requant_weight_rowwise_fp8_cached), fused into one pass: the BF16
 // intermediate y = bf16(fl(e4m3(w)*S)) is formed in registers, never stored.
-// CPT 16-byte chunks (16 codes each, inside one 128-column block) per thread.
+// The row absmax is taken over the F32 products before their BF16 rounding:
+// rounding is monotonic and sign-symmetric, so max|bf16(p)| = bf16(max|p|).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void bf16_pair(f32x2 e, float scale, float *y)
+
+// Eight F32 products e4m3(code)*scale of the codes in dword pair (w0, w1)
+// (two codes per converter call, exactly), then their BF16 pairs.
+__device__ __forceinline__ void blockfp8_products(uint32_t w0, uint32_t w1, float scale,
+                                                  float *p)
 {
-    // times the block scale (one f32 rounding), then to BF16 (RNE), back to f32
-    bf16x2 b = (bf16x2){(__bf16)(e[0] * scale), (__bf16)(e[1] * scale)};
-    uint32_t bits = __builtin_bit_cast(uint32_t, b);
-    y[0] = bf16_lo(bits);
-    y[1] = bf16_hi(bits);
+    const f32x2 e0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const f32x2 e1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const f32x2 e2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const f32x2 e3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    p[0] = e0[0] * scale; p[1] = e0[1] * scale;
+    p[2] = e1[0] * scale; p[3] = e1[1] * scale;
+    p[4] = e2[0] * scale; p[5] = e2[1] * scale;
+    p[6] = e3[0] * scale; p[7] = e3[1] * scale;
 }
 
-__device__ __forceinline__ void blockfp8_to_bf16_vals(u32x4 raw, float scale, float *y)
+// RNE of a binary32 to BF16 and back (the BF16 intermediate of one value).
+__device__ __forceinline__ float bf16_round(float v)
 {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        // two E4M3 codes per converter call, exactly
-        bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false), scale, &y[4 * w]);
-        bf16_pair(__builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true), scale, &y[4 * w + 2]);
-    }
+    return bf16_lo(pk_bf16(v, 0.0f));
 }
 
-template <int CPT>
-__global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise(
-    const uint8_t *__restrict__ w, const float *__restrict__ grid,
-    uint8_t *__restrict__ q, float *__restrict__ s, uint32_t k)
-{
-    __shared__ float red[4];
-    const uint32_t row = blockIdx.x;
-    const uint8_t *wr = w + (size_t)row * k;
-    const float *gr = grid + (size_t)(row / 128) * (k / 128);
-    const uint32_t nch = k / 16;
-    float y[CPT][16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        uint32_t c = threadIdx.x + 256u * j;
-        u32x4 raw = {0, 0, 0, 0};
-        float scale = 0.0f;
-        if (c < nch) {
-            raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr + (size_t)c * 16));
-            scale = gr[(c * 16) / 128];
-        }
-        blockfp8_to_bf16_vals(raw, scale, y[j]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(y[j][i]));
-    }
-    amax = block_max_256(amax, red);
-    const float sc = div_rn(amax, 448.0f);
-    const ScaleDiv dv(sc);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        uint32_t c = threadIdx.x + 256u * j;
-        if (c < nch) {
-            u32x2 lo = enc8_e4m3(&y[j][0], dv, sc == 0.0f), hi = enc8_e4m3(&y[j][8], dv, sc == 0.0f);
-            u32x4 o = {lo[0], lo[1], hi[0], hi[1]};
-            *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = o;
-        }
-    }
-    if (threadIdx.x == 0)
-        s[row] = sc;
-}
-
+// Long rows: a workgroup per row, two passes over global memory.
 __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_long(
     const uint8_t *__restrict__ w, const float *__restrict__ grid,
     uint8_t *__restrict__ q, float *__restrict__ s, uint32_t k)
@@ -455,33 +516,42 @@ __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_long(
     const float *gr = grid + (size_t)(row / 128) * (k / 128);
     const uint32_t nch = k / 16;
     float amax = 0.0f;
-    float y[16];
     for (uint32_t c = threadIdx.x; c < nch; c += 256) {
-        u32x4 raw = *reinterpret_cast<const u32x4 *>(wr + (size_t)c * 16);
-        blockfp8_to_bf16_vals(raw, gr[(c * 16) / 128], y);
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(wr + (size_t)c * 16);
+        const float bs = gr[(c * 16) / 128];
+        float p[16];
+        blockfp8_products(raw[0], raw[1], bs, &p[0]);
+        blockfp8_products(raw[2], raw[3], bs, &p[8]);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(y[i]));
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(p[i]));
     }
-    amax = block_max_256(amax, red);
-    const float sc = div_rn(amax, 448.0f);
+    amax = bf16_round(block_max_256(amax, red));
+    const float sc = div_by_const<448>(amax);
     const ScaleDiv dv(sc);
     for (uint32_t c = threadIdx.x; c < nch; c += 256) {
-        u32x4 raw = *reinterpret_cast<const u32x4 *>(wr + (size_t)c * 16);
-        blockfp8_to_bf16_vals(raw, gr[(c * 16) / 128], y);
-        u32x2 lo = enc8_e4m3(&y[0], dv, sc == 0.0f), hi = enc8_e4m3(&y[8], dv, sc == 0.0f);
-        u32x4 o = {lo[0], lo[1], hi[0], hi[1]};
-        *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = o;
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(wr + (size_t)c * 16);
+        const float bs = gr[(c * 16) / 128];
+        float y[16];
+        blockfp8_products(raw[0], raw[1], bs, &y[0]);
+        blockfp8_products(raw[2], raw[3], bs, &y[8]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            y[i] = bf16_round(y[i]);
+        u32x4 o = {0, 0, 0, 0};
+        if (sc != 0.0f) {
+            const u32x2 lo = dv.fast ? enc8_e4m3_path<true>(&y[0], dv) : enc8_e4m3_path<false>(&y[0], dv);
+            const u32x2 hi = dv.fast ? enc8_e4m3_path<true>(&y[8], dv) : enc8_e4m3_path<false>(&y[8], dv);
+            o = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+        }
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16));
     }
     if (threadIdx.x == 0)
         s[row] = sc;
 }
 
-// Rows of up to 64*CPL chunks: one wave per row (four rows per workgroup),
-// CPL 16-code chunks per lane in registers, the row absmax by wave shuffles
-// alone (no LDS, no barrier), every load / store instruction one contiguous
-// kilobyte (lane l takes chunks l, l + 64, ...), and the BF16 intermediate
-// kept packed (two values per register).
+// Rows of up to 64*CPL 16-code chunks: one wave per row, the BF16
+// intermediate kept packed (two values per register) between the passes.
 template <int CPL>
 __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_wave(
     const uint8_t *__restrict__ w, const float *__restrict__ grid,
@@ -510,17 +580,18 @@ __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_wave(
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        float y[16];
-        blockfp8_to_bf16_vals(raw[j], bs[j], y);
+        float p[16];
+        blockfp8_products(raw[j][0], raw[j][1], bs[j], &p[0]);
+        blockfp8_products(raw[j][2], raw[j][3], bs[j], &p[8]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            yb[j][i] = (__float_as_uint(y[2 * i]) >> 16) | (__float_as_uint(y[2 * i + 1]) & 0xFFFF0000u);
-            amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(y[2 * i]),
-                                                         __builtin_fabsf(y[2 * i + 1])));
+            yb[j][i] = pk_bf16(p[2 * i], p[2 * i + 1]);
+            amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(p[2 * i]),
+                                                         __builtin_fabsf(p[2 * i + 1])));
         }
     }
-    amax = wave_max(amax);
-    const float sc = div_rn(amax, 448.0f);
+    amax = bf16_round(wave_max(amax));
+    const float sc = div_by_const<448>(amax);
     const ScaleDiv dv(sc);
     // The scale is one per row (wave-uniform): pick the division path once.
     auto encode = [&](auto fast_tag) {
@@ -541,7 +612,7 @@ __global__ __launch_bounds__(256) void k_requant_blockfp8_rowwise_wave(
                     const u32x2 hi = enc8_e4m3_path<FAST>(&v[8], dv);
                     o = (u32x4){lo[0], lo[1], hi[0], hi[1]};
                 }
-                *reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16) = o;
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(q + (size_t)row * k + (size_t)c * 16));
             }
         }
     };
@@ -559,18 +630,16 @@ hipError_t launch_requant_blockfp8_rowwise(const uint8_t *w, const float *grid,
 {
     const uint32_t nch = k / 16;
     const dim3 gw((n + 3) / 4), b(256);
-    if (nch <= 64 * 2)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<2>, gw, b, 0, st, w, grid, q, s, n, k);
-    else if (nch <= 64 * 4)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<4>, gw, b, 0, st, w, grid, q, s, n, k);
-    else if (nch <= 64 * 6)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<6>, gw, b, 0, st, w, grid, q, s, n, k);
-    else if (nch <= 64 * 8)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<8>, gw, b, 0, st, w, grid, q, s, n, k);
-    else if (nch <= 1024)
-        hipLaunchKernelGGL(k_requant_blockfp8_rowwise<4>, dim3(n), b, 0, st, w, grid, q, s, k);
+#define QP_BF8_WAVE(C)                                                                            \
+    else if (nch <= 64u * C) hipLaunchKernelGGL(k_requant_blockfp8_rowwise_wave<C>, gw, b, 0, st, \
+                                                 w, grid, q, s, n, k);
+    if (false) {
+    }
+    QP_BF8_WAVE(2) QP_BF8_WAVE(4) QP_BF8_WAVE(5) QP_BF8_WAVE(6) QP_BF8_WAVE(8) QP_BF8_WAVE(12)
+    QP_BF8_WAVE(16)
     else
         hipLaunchKernelGGL(k_requant_blockfp8_rowwise_long, dim3(n), b, 0, st, w, grid, q, s, k);
+#undef QP_BF8_WAVE
     count_launch();
     return hipGetLastError();
 }

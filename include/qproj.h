@@ -137,6 +137,20 @@ int int8_gemm_block_partials(const int8_t *a_i8, const int8_t *w_i8,
                              int32_t *p, uint32_t m, uint32_t n, uint32_t k,
                              void *stream);
 
+/* Test export: the device encoders of the quantizer kernels applied to n
+ * arbitrary binary32 values y (n % 8 == 0, n <= 2^30), one code per output
+ * byte (E2M1 codes in the low nibble, int8 codes as two's-complement bytes).
+ * Domains: E4M3_NOSAT |y| < 464; E2M1_NOSAT |y| <= 8; INT8 |y| < 127.5;
+ * E4M3 and E2M1 (saturating first) any finite y; E4M3_SCALE finite y >= 0
+ * (the NVFP4 block-scale encoder).  Outside its domain an encoder's output
+ * is unspecified.  Rounding: to nearest, ties to the even code; a value
+ * that rounds to zero keeps its sign. */
+enum qp_encoder {
+    QP_ENC_E4M3_NOSAT = 0, QP_ENC_E2M1_NOSAT = 1, QP_ENC_INT8 = 2,
+    QP_ENC_E4M3 = 3, QP_ENC_E2M1 = 4, QP_ENC_E4M3_SCALE = 5
+};
+int qproj_encode_test(int kind, const float *y, uint8_t *out, uint32_t n, void *stream);
+
 /* ------------------------------------------------------------------------
  * BF16 -> NVFP4 quantizer (gemm_fp4.rs, quantize_bf16_to_nvfp4).
  *   x       [rows, k]    BF16

@@ -66,6 +66,7 @@ def lib():
         L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         L.oracle_bf16_to_float.restype = F
         L.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
+        L.oracle_encode_array.argtypes = [ctypes.c_int, P, P, I]
         L.oracle_requant_a_bf16_int8.argtypes = [P, P, P, I, I]
         L.oracle_requant_w_nvfp4_int8.argtypes = [P, P, F, P, P, I, I]
         L.oracle_quantize_bf16_nvfp4.argtypes = [P, P, P, F, I, I]
@@ -126,6 +127,19 @@ def e4m3_encode(y: float) -> int:
 
 def int8_encode(y: float) -> int:
     return int(lib().oracle_int8_encode(float(y)))
+
+
+ENC_E4M3, ENC_E2M1, ENC_INT8 = 0, 1, 2
+
+
+def encode_array(kind: int, y) -> np.ndarray:
+    """The scalar encoders over a float32 array: E4M3 (kind 0) or E2M1
+    (kind 1) code bytes, or int8 codes as their two's-complement bytes
+    (kind 2)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().oracle_encode_array(int(kind), y.ctypes.data, out.ctypes.data, y.size)
+    return out
 
 
 def bf16_from_double(x: float) -> int:

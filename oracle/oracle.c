@@ -120,6 +120,17 @@ int8_t oracle_int8_encode(float y)
     return (int8_t)r;
 }
 
+/* The three encoders above over an array (one code per byte; E2M1 codes in
+ * the low nibble), for checks that sweep many values at once. */
+void oracle_encode_array(int kind, const float *y, uint8_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = kind == 0 ? oracle_e4m3_encode(y[i])
+               : kind == 1 ? oracle_e2m1_encode(y[i])
+                           : (uint8_t)oracle_int8_encode(y[i]);
+}
+
 float oracle_bf16_to_float(uint16_t b)
 {
     uint32_t u = (uint32_t)b << 16;

@@ -107,6 +107,64 @@ def test_e2m1_codes_over_every_bf16_input_at_unit_scale():
         f"got {got[tuple(bad[0])]:#04x} oracle {op[tuple(bad[0])]:#04x}"
 
 
+# ---------------------------------------- the encoders on binary32 values
+# The quotients the kernels encode are arbitrary binary32 values, so the
+# device encoders are also driven directly (test export qproj_encode_test):
+# every binary32 value within 64 ulps of each grid point and each midpoint,
+# a strided sample (every 997th bit pattern) of the whole domain, both
+# signs and both zeros, against the oracle's encoders.
+def _f32_bits(v):
+    return np.asarray(v, np.float32).view(np.uint32).astype(np.int64)
+
+
+def _around(points, ulps=64):
+    """Every non-negative binary32 within `ulps` of each point."""
+    u = _f32_bits(points)[:, None] + np.arange(-ulps, ulps + 1)[None, :]
+    u = u[(u >= 0) & (u < 0x7F800000)]
+    return np.unique(u).astype(np.uint32).view(np.float32)
+
+
+def _domain(grid, limit, strict):
+    """Grid points, midpoints, their neighbourhoods and a strided sample of
+    [0, limit) (or [0, limit]), both signs."""
+    g = np.asarray(grid, np.float64)
+    pts = np.concatenate([g, (g[:-1] + g[1:]) / 2, [limit]])
+    vals = np.concatenate([_around(pts.astype(np.float32)),
+                           np.arange(0, int(_f32_bits([limit])[0]), 997,
+                                     dtype=np.int64).astype(np.uint32).view(np.float32)])
+    vals = vals[(vals < limit) if strict else (vals <= limit)]
+    vals = np.unique(vals)
+    vals = np.concatenate([vals, -vals, np.array([-0.0], np.float32)])
+    pad = (-len(vals)) % 8
+    return np.concatenate([vals, np.zeros(pad, np.float32)]).astype(np.float32)
+
+
+E4M3_GRID = [oracle.e4m3_decode(c) for c in range(0x7F)]
+E2M1_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+INT8_GRID = list(range(128))
+
+
+@pytest.mark.parametrize("kind,okind,grid,limit,strict", [
+    (qp.QP_ENC_E4M3_NOSAT, oracle.ENC_E4M3, E4M3_GRID, 464.0, True),
+    (qp.QP_ENC_E4M3, oracle.ENC_E4M3, E4M3_GRID + [464.0, 480.0, 1e6], 3.0e38, False),
+    (qp.QP_ENC_E2M1_NOSAT, oracle.ENC_E2M1, E2M1_GRID + [8.0], 8.0, False),
+    (qp.QP_ENC_E2M1, oracle.ENC_E2M1, E2M1_GRID + [8.0, 1e3], 3.0e38, False),
+    (qp.QP_ENC_INT8, oracle.ENC_INT8, INT8_GRID, 127.5, True),
+    (qp.QP_ENC_E4M3_SCALE, oracle.ENC_E4M3, E4M3_GRID + [464.0, 1e6], 3.0e38, False),
+], ids=["e4m3", "e4m3_sat", "e2m1", "e2m1_sat", "int8", "e4m3_scale"])
+def test_device_encoders_on_binary32_boundaries(kind, okind, grid, limit, strict):
+    y = _domain(grid, limit, strict)
+    if kind == qp.QP_ENC_E4M3_SCALE:
+        y = np.abs(y)                    # block scales are never negative
+    out = empty((len(y),), torch.uint8)
+    qp.encode_test(kind, dev(torch.from_numpy(y)), out)
+    got = host(out)
+    want = oracle.encode_array(okind, y)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} of {len(y)} differ; first y = {y[bad[0]]!r} " \
+        f"({_f32_bits([y[bad[0]]])[0]:#010x}): got {got[bad[0]]:#04x}, oracle {want[bad[0]]:#04x}"
+
+
 # ------------------------------------------------- hand-worked blocks on the GPU
 def _cases():
     cp = configparser.ConfigParser()

@@ -80,11 +80,14 @@ def test_quantize_bf16_nvfp4_bit_exact(rows, k, scale2):
     assert np.array_equal(host(p), op)
 
 
-# k / 8 chunks of 16 bytes per row select the kernel: <= 256, 512, 768,
-# 1024, 2048 chunks per workgroup, or the long-row loop; each is run full
-# and ragged (k = 2064, 6160, 12304 leave part of the last chunk round empty).
-@pytest.mark.parametrize("rows,k", [(1, 16), (7, 48), (40, 5120), (3, 20000), (9, 2064),
-                                    (3, 8192), (2, 6160), (3, 16384), (2, 12304)])
+# k / 8 chunks of 16 bytes per row select the kernel: one wave per row with
+# up to 1, 2, 4, 6, 8, 10, 12 or 16 chunks per lane, a workgroup per row with
+# up to 8 chunks per thread, or the two-pass long-row loop; each is run
+# full and ragged (k = 1552, 2064, 6160, 12304 leave part of the last round
+# empty), with row counts that leave the last workgroup's waves partly idle.
+@pytest.mark.parametrize("rows,k", [(1, 16), (7, 48), (5, 1024), (6, 1552), (9, 2064),
+                                    (4, 4096), (40, 5120), (3, 6144), (2, 6160), (3, 8192),
+                                    (2, 12304), (3, 16384), (3, 20000)])
 def test_quant_rowwise_fp8_bit_exact(rows, k):
     x = _with_edges(_bf16_rows((rows, k), 31 + rows, std=0.02))
     q, s = empty((rows, k), torch.uint8), empty((rows,), torch.float32)
@@ -95,14 +98,13 @@ def test_quant_rowwise_fp8_bit_exact(rows, k):
 
 
 @pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 5120), (1152, 1024),
-                                 (640, 8192), (256, 2176), (128, 8320), (128, 16384),
-                                 (128, 16512), (256, 24576)])
+                                 (640, 8192), (256, 2176), (256, 5888), (128, 8320),
+                                 (128, 16384), (128, 16512), (256, 24576)])
 def test_requant_blockfp8_rowwise_bit_exact(n, k):
-    # k / 16 / 64 chunks per lane: 1 (partly and wholly used), 5, 8, and 3
-    # with the third partly used; the row-pipelined kernel takes several rows
-    # per wave once n exceeds its resident waves.  Longer rows take the
-    # workgroup-per-row kernel (k = 8320 just past the wave kernels, 16384 at
-    # its end) and the long-row loop (16512, 24576).
+    # k / 16 chunks per row select a one-wave-per-row kernel with up to 2, 4,
+    # 5, 6, 8, 12 or 16 chunks per lane (k = 128 and 384 leave most lanes
+    # idle, 2176, 5888 and 8320 part of the last round) or, past 16384, the
+    # two-pass workgroup-per-row loop (16512, 24576).
     cse = synth.fp8_block("cpu", m=1, n=n, k=k)
     w, grid = cse.w_block.clone(), cse.block_grid
     w[1, ::5] = 0x80                     # -0.0 codes
