@@ -21,8 +21,9 @@ The same line carries:
                 the block-scaled FP8 GEMV (128 x 128 F32 block scales)
                 at the decode shapes for M in {1, 2, 4}, and the NVFP4-weight
                 GEMV (W4A16) there for M in {1, 2, 8}, in GB/s;
-  ablations     the W4A4 GEMM under three workgroup -> tile orders, and a
-                tile GEMM against the GEMV at M = 8 on the lm_head weight.
+  ablations     the W4A4 GEMM under three workgroup -> tile orders, a tile
+                GEMM against the GEMV at M = 8 on the lm_head weight, and
+                the int8 GEMM's two operand routes (int8 MFMA, FP16 MFMA).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
 """
@@ -408,7 +409,7 @@ def run_secondary(qp, synth, dev, only):
 
     # W4A8 prefill: NVFP4 weight 17408x5120 -> int8; acts 2048x5120.
     if want("w4a8") or want("requant_a_bf16_int8") or want("requant_w_nvfp4_int8") \
-            or want("int8_gemm_blockscaled"):
+            or want("int8_gemm_blockscaled") or want("ablations") or want("int8_operand_route"):
         m, n, k = 2048, 17408, 5120
         c = synth.w4a8_prefill(dev, m, n, k)
         wp = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
@@ -434,6 +435,19 @@ def run_secondary(qp, synth, dev, only):
                    lambda p, e, q, s: qp.requant_w_nvfp4_int8(p, e, 1.0, q, s))
         gemm_item("int8_gemm_blockscaled", 2 * m * n * k,
                   lambda: qp.int8_gemm_blockscaled(a_i8, w_i8, a_s, w_s, out), "int8")
+        # Operand-route ablation (gemm_dense_int8.rs, int8_gemm_faith2_prefill):
+        # the same GEMM with P_b on FP16 MFMA over converted operands, which
+        # halves the fold's vector-ALU work and doubles the matrix core's.
+        if want("ablations") or want("int8_operand_route"):
+            routes = {}
+            for name, fn in (("int8_mfma", qp.int8_gemm_blockscaled),
+                             ("fp16_mfma", qp.int8_gemm_blockscaled_f16ops)):
+                ms = time_launches(lambda i: fn(a_i8, w_i8, a_s, w_s, out), iters=10)
+                tf = 2 * m * n * k / (ms * 1e-3) / 1e12
+                routes[name] = {"us": round(ms * 1e3, 1), "TOPs": round(tf, 1),
+                                "frac_int8": round(tf / PEAK_TFLOPS["int8"], 4)}
+                log(f"  ablation int8 operands {name}: {ms*1e3:.1f} us  {tf:.1f} TOP/s")
+            res["ablation_int8_operand_route"] = {"shape": [m, n, k], "routes": routes}
         del wp, we, w_i8, w_s, a_i8, a_s, out
         torch.cuda.empty_cache()
 

@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "requant_w_nvfp4_int8": [P, P, F, P, P, U, U, P],
             "requant_a_bf16_int8": [P, P, P, U, U, P],
             "int8_gemm_blockscaled": [P, P, P, P, P, U, U, U, P],
+            "int8_gemm_blockscaled_f16ops": [P, P, P, P, P, U, U, U, P],
             "int8_w4a8_prefill": [P, P, P, P, P, P, U, U, U, P],
             "int8_w4a8_prefill_noalloc": [P, P, P, P, U, U, U, P],
             "qproj_encode_test": [I, P, P, U, P],
@@ -196,6 +197,21 @@ def int8_gemm_blockscaled(a_i8, w_i8, a_scale, w_scale, out, stream=None):
     _need(w_scale, "w_scale", F32, (n, k // 32))
     _need(out, "out", BF16, (m, n))
     _check("int8_gemm_blockscaled", lib().int8_gemm_blockscaled(
+        _ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
+        m, n, k, _stream(stream)))
+
+
+def int8_gemm_blockscaled_f16ops(a_i8, w_i8, a_scale, w_scale, out, stream=None):
+    """The operand-route ablation of int8_gemm_blockscaled (FP16 MFMA on
+    converted operands; bit-identical output; k % 128 == 0)."""
+    m, k = a_i8.shape
+    n = w_i8.shape[0]
+    _need(a_i8, "a_i8", I8, (m, k))
+    _need(w_i8, "w_i8", I8, (n, k))
+    _need(a_scale, "a_scale", F32, (m, k // 32))
+    _need(w_scale, "w_scale", F32, (n, k // 32))
+    _need(out, "out", BF16, (m, n))
+    _check("int8_gemm_blockscaled_f16ops", lib().int8_gemm_blockscaled_f16ops(
         _ptr(a_i8), _ptr(w_i8), _ptr(a_scale), _ptr(w_scale), _ptr(out),
         m, n, k, _stream(stream)))
 

@@ -115,6 +115,20 @@ int int8_w4a8_prefill(const uint16_t *a_bf16, const int8_t *w_i8,
                                      out, nullptr, m, n, k, S(stream)));
 }
 
+int int8_gemm_blockscaled_f16ops(const int8_t *a_i8, const int8_t *w_i8,
+                                 const float *a_scale, const float *w_scale,
+                                 uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                 void *stream)
+{
+    if (int e = check_ptrs({a_i8, w_i8, a_scale, w_scale, out}))
+        return e;
+    if (m == 0 || n == 0 || k == 0 || k % 128 != 0 || !fits(m, k) || !fits(n, k) ||
+        !fits(m, n))
+        return QP_ERR_SHAPE;
+    return done(qp::launch_int8_gemm_f16ops(a_i8, w_i8, a_scale, w_scale, out, m, n, k,
+                                            S(stream)));
+}
+
 int int8_gemm_block_partials(const int8_t *a_i8, const int8_t *w_i8, int32_t *p,
                              uint32_t m, uint32_t n, uint32_t k, void *stream)
 {

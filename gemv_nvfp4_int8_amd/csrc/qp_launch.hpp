@@ -33,6 +33,10 @@ hipError_t launch_w4a16_gemv(const uint16_t *x, const uint8_t *wp, const uint8_t
 hipError_t launch_int8_gemm(const int8_t *a, const int8_t *w, const float *as,
                             const float *ws, uint16_t *out, int32_t *partials,
                             uint32_t m, uint32_t n, uint32_t k, hipStream_t st);
+// The operand-route ablation: the same GEMM on FP16 MFMA (k % 128 == 0).
+hipError_t launch_int8_gemm_f16ops(const int8_t *a, const int8_t *w, const float *as,
+                                   const float *ws, uint16_t *out, uint32_t m, uint32_t n,
+                                   uint32_t k, hipStream_t st);
 hipError_t launch_fp8_gemm_rowscale(const uint8_t *a, const float *as,
                                     const uint8_t *w, const float *ws,
                                     uint16_t *out, uint32_t m, uint32_t n,

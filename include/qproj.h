@@ -112,6 +112,19 @@ int int8_w4a8_prefill(const uint16_t *a_bf16, const int8_t *w_i8,
                       float *a_scale_scratch, uint16_t *out,
                       uint32_t m, uint32_t n, uint32_t k, void *stream);
 
+/* Ablation export: int8_gemm_blockscaled with the int8 operands converted
+ * to FP16 in LDS and P_b formed on FP16 MFMA (exact: int8 values and block
+ * partial sums are integers FP16 and F32 hold exactly), the fold one FMA per
+ * output and block.  Same arguments and bit-identical output; requires
+ * k % 128 == 0.  Measured slower than the int8-MFMA kernel on the prefill
+ * shape, it is kept to time the two operand routes side by side
+ * (gemm_dense_int8.rs, int8_gemm_faith2_prefill: int8 x int8 with per-32
+ * block scales). */
+int int8_gemm_blockscaled_f16ops(const int8_t *a_i8, const int8_t *w_i8,
+                                 const float *a_scale, const float *w_scale,
+                                 uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                 void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * call as int8_w4a8_prefill, same kernels and bit-identical output, with the

@@ -234,6 +234,8 @@ _EXTENT_CALLS = {
         FAKE, FAKE2, FAKE, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
     "int8_w4a8_prefill_noalloc": (lambda m, n, k: L.int8_w4a8_prefill_noalloc(
         FAKE, FAKE2, FAKE, FAKE2, m, n, k, None), (4, 256, 256)),
+    "int8_gemm_blockscaled_f16ops": (lambda m, n, k: L.int8_gemm_blockscaled_f16ops(
+        FAKE, FAKE2, FAKE, FAKE2, FAKE, m, n, k, None), (4, 256, 256)),
     "int8_gemm_block_partials": (lambda m, n, k: L.int8_gemm_block_partials(
         FAKE, FAKE2, FAKE, m, n, k, None), (4, 256, 256)),
     "quantize_bf16_nvfp4": (lambda r, k: L.quantize_bf16_nvfp4(
@@ -331,6 +333,8 @@ _PTR_CALLS = {
         p[0], p[1], p[2], p[3], p[4], p[5], 4, 256, 256, None), 6),
     "int8_w4a8_prefill_noalloc": (lambda p: L.int8_w4a8_prefill_noalloc(
         p[0], p[1], p[2], p[3], 4, 256, 256, None), 4),
+    "int8_gemm_blockscaled_f16ops": (lambda p: L.int8_gemm_blockscaled_f16ops(
+        p[0], p[1], p[2], p[3], p[4], 4, 256, 256, None), 5),
     "int8_gemm_block_partials": (lambda p: L.int8_gemm_block_partials(
         p[0], p[1], p[2], 4, 256, 256, None), 3),
     "quantize_bf16_nvfp4": (lambda p: L.quantize_bf16_nvfp4(p[0], p[1], p[2], 1.0, 4, 256, None), 3),
@@ -388,3 +392,11 @@ def test_noalloc_prefill_refuses_problems_beyond_its_scratch_array():
         == qp.QP_ERR_SCRATCH
     assert qp.launch_count() == before
     assert qp.status_string(qp.QP_ERR_SCRATCH) != "unknown status"
+
+
+def test_f16_operand_route_needs_k_multiple_of_128():
+    before = qp.launch_count()
+    for k in (32, 64, 96, 160, 192):
+        assert L.int8_gemm_blockscaled_f16ops(FAKE, FAKE2, FAKE, FAKE2, FAKE, 256, 128, k,
+                                              None) == qp.QP_ERR_SHAPE
+    assert qp.launch_count() == before

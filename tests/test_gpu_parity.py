@@ -161,7 +161,11 @@ def test_w4a8_tiny_pipeline_matches_oracle():
     assert_gemm_close(host(out), oracle.int8_gemm_blockscaled(oa, ow, oas, ows), "w4a8 tiny")
 
 
-@pytest.mark.parametrize("m,n,k", [(130, 200, 96), (256, 384, 1024), (7, 64, 5120)])
+# Ragged M and N tails, one and several tiles, K of one block up to the
+# prefill's 5120.
+@pytest.mark.parametrize("m,n,k", [(130, 200, 96), (256, 384, 1024), (7, 64, 5120),
+                                   (256, 128, 64), (300, 200, 640), (513, 161, 192),
+                                   (1024, 1056, 2048)])
 def test_int8_gemm_blockscaled_ragged(m, n, k):
     a = _bf16_rows((m, k), 41 + m, outliers=0.01)
     w = _bf16_rows((n, k), 42 + n, std=0.02)
@@ -171,6 +175,47 @@ def test_int8_gemm_blockscaled_ragged(m, n, k):
     qp.int8_gemm_blockscaled(dev(torch.from_numpy(oa)), dev(torch.from_numpy(ow)),
                              dev(torch.from_numpy(oas)), dev(torch.from_numpy(ows)), out)
     assert_gemm_close(host(out), oracle.int8_gemm_blockscaled(oa, ow, oas, ows), f"int8 {m}x{n}x{k}")
+
+
+def _fold_in_f32(p, sa, sw):
+    """The GEMM's F32 fold of exact block partials p [m, n, nb], written out:
+    acc = fma(P_b, fl(a_s * w_s), acc) for b = 0, 1, ... in K order, each FMA
+    one binary32 rounding (emulated exactly: P_b * sc is exact in binary64,
+    and the sum is rounded once with a midpoint correction), then BF16."""
+    from tests.test_division_shortcut import _rn32_of_sum
+    m, n, nb = p.shape
+    acc = np.zeros((m, n), np.float64)
+    for b in range(nb):
+        sc = (sa[:, b][:, None] * sw[:, b][None, :]).astype(np.float32)
+        acc = _rn32_of_sum(p[:, :, b].astype(np.float64) * sc.astype(np.float64), acc)
+    return bits(torch.from_numpy(acc.astype(np.float32)).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("m,n,k", [(130, 200, 96), (256, 128, 128), (300, 200, 640),
+                                   (513, 161, 384)])
+def test_int8_gemm_is_the_f32_fold_of_the_exact_partials(m, n, k):
+    """The GEMM (int8 MFMA) and its operand-route ablation (FP16 MFMA on
+    converted operands, for K % 128 == 0) both return, bit for bit, bf16 of
+    the F32 FMA chain over the exact int32 block partials in K order, with
+    each scale product a binary32 multiply."""
+    a = _bf16_rows((m, k), 61 + m, outliers=0.01)
+    w = _bf16_rows((n, k), 62 + n, std=0.02)
+    oa, oas = oracle.requant_a_bf16_int8(bits(a))
+    ow, ows = oracle.requant_a_bf16_int8(bits(w))
+    t = lambda x: dev(torch.from_numpy(x))
+    p = empty((m, n, k // 32), torch.int32)
+    qp.int8_gemm_block_partials(t(oa), t(ow), p)
+    pp = host(p)
+    assert np.array_equal(pp, oracle.int8_block_partials(oa, ow))
+    want = _fold_in_f32(pp, oas, ows)
+    out = filled((m, n), torch.bfloat16)
+    qp.int8_gemm_blockscaled(t(oa), t(ow), t(oas), t(ows), out)
+    assert np.array_equal(host(out), want)
+    if k % 128 == 0:
+        # the operand-route ablation (FP16 MFMA on converted operands)
+        out = filled((m, n), torch.bfloat16)
+        qp.int8_gemm_blockscaled_f16ops(t(oa), t(ow), t(oas), t(ows), out)
+        assert np.array_equal(host(out), want)
 
 
 # Shapes cover both kernels: the 128 x 128 one and the 256 x 160 one (M >= 256,
