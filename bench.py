@@ -653,6 +653,86 @@ def cpu_baseline(synth, gemv_seconds=12.0, item_seconds=1.2):
     b, t = run(frac)
     gbs = b / t / 1e9
     log(f"cpu oracle: {t:.1f} s on {threads} threads, {gbs:.4f} GB/s (fraction {frac:.4f})")
+    def oracle_per_config(synth, target_s):
+        """The oracle on each workload's steps other than the headline GEMV,
+        every input built as the GPU rows build it; each step is timed on the
+        first `u` rows of the input its cost scales with (activation rows for
+        the GEMMs), u sized from a probe to take about target_s."""
+        import numpy as np
+        import oracle
+        bits = synth.to_numpy_bits
+        res = {}
+
+        def item(name, unit, full, work, run, what):
+            u = max(1, full // 2048)
+            t0 = time.perf_counter()
+            run(u)
+            t = time.perf_counter() - t0
+            u = int(min(full, max(u, u * target_s / max(t, 1e-4))))
+            t0 = time.perf_counter()
+            run(u)
+            t = time.perf_counter() - t0
+            rate = work(u) / t / 1e9
+            res[name] = {"value": round(rate, 4), "unit": unit, "seconds": round(t, 3),
+                         "sample": f"{what} {u} of {full}"}
+            log(f"cpu oracle {name}: {rate:.4g} {unit} ({what} {u} of {full}, {t:.2f} s)")
+
+        # W4A8 tiny (N=256, K=512, M=16), whole: requant_w + requant_a + GEMM.
+        c = synth.w4a8_tiny("cpu")
+        wp0, we0, a0 = bits(c.w_packed), bits(c.w_e4m3), bits(c.a_bf16)
+
+        def tiny(_):
+            wq, wsc = oracle.requant_w_nvfp4_int8(wp0, we0, c.scale2)
+            aq, asc = oracle.requant_a_bf16_int8(a0)
+            oracle.int8_gemm_blockscaled(aq, wq, asc, wsc)
+        item("w4a8_tiny_step", "GFLOP/s", 1, lambda u: 2 * 16 * 256 * 512, tiny, "whole step,")
+
+        # W4A8 prefill: NVFP4 weight 17408x5120 -> int8; acts 2048x5120.
+        m, n, k = 2048, 17408, 5120
+        c = synth.w4a8_prefill("cpu", m, n, k)
+        wb, ab = bits(c.w_bf16), bits(c.a_bf16)
+        wp, we = oracle.quantize_bf16_nvfp4(wb, c.scale2)
+        wq, wsc = oracle.requant_w_nvfp4_int8(wp, we, c.scale2)
+        aq, asc = oracle.requant_a_bf16_int8(ab)
+        item("requant_a_bf16_int8", "GB/s", m, lambda u: u * k * 2 + u * k + u * (k // 32) * 4,
+             lambda u: oracle.requant_a_bf16_int8(ab[:u]), "activation rows")
+        item("requant_w_nvfp4_int8", "GB/s", n,
+             lambda u: u * (k // 2 + k // 16 + k + (k // 32) * 4),
+             lambda u: oracle.requant_w_nvfp4_int8(wp[:u], we[:u], c.scale2), "weight rows")
+        item("int8_gemm_blockscaled", "GFLOP/s", m, lambda u: 2 * u * n * k,
+             lambda u: oracle.int8_gemm_blockscaled(aq[:u], wq, asc[:u], wsc), "activation rows")
+        del c, wb, ab, wp, we, wq, wsc, aq, asc
+
+        # W4A4 prefill: acts 4096x17408 -> NVFP4; NVFP4 weight 5120x17408.
+        m, n, k = 4096, 5120, 17408
+        c = synth.w4a4_prefill("cpu", m, n, k)
+        ab = bits(c.a_bf16)
+        wp, wsc = oracle.quantize_bf16_nvfp4(bits(c.w_bf16), c.scale_w2)
+        ap, asc = oracle.quantize_bf16_nvfp4(ab[:64], 1.0)
+        item("quantize_bf16_nvfp4", "GB/s", m, lambda u: u * (k * 2 + k // 2 + k // 16),
+             lambda u: oracle.quantize_bf16_nvfp4(ab[:u], 1.0), "activation rows")
+        item("w4a4_gemm", "GFLOP/s", 64, lambda u: 2 * u * n * k,
+             lambda u: oracle.w4a4_gemm(ap[:u], asc[:u], wp, wsc, 1.0, c.scale_w2),
+             "activation rows (of the first 64)")
+        del c, ab, wp, wsc, ap, asc
+
+        # Block-FP8 -> row-wise FP8 requant + GEMM: W 12288x5120, acts 8192x5120.
+        m, n, k = 8192, 12288, 5120
+        c = synth.fp8_block("cpu", m, n, k)
+        w, grid = bits(c.w_block), c.block_grid.numpy()
+        ab = bits(c.a_bf16)
+        item("requant_w_blockfp8_rowwise", "GB/s", n // 128, lambda u: 128 * u * (2 * k + 4),
+             lambda u: oracle.requant_w_blockfp8_rowwise(w[:128 * u], grid[:u]),
+             "128-row weight blocks")
+        wq, wsc = oracle.requant_w_blockfp8_rowwise(w, grid)
+        aq, asc = oracle.quant_rowwise_fp8(ab[:256])
+        item("quant_rowwise_fp8", "GB/s", m, lambda u: u * (3 * k + 4),
+             lambda u: oracle.quant_rowwise_fp8(ab[:u]), "activation rows")
+        item("fp8_gemm_rowscale", "GFLOP/s", 256, lambda u: 2 * u * n * k,
+             lambda u: oracle.fp8_gemm_rowscale(aq[:u], asc[:u], wq, wsc),
+             "activation rows (of the first 256)")
+        return res
+
     per = oracle_per_config(synth, item_seconds)
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": round(t, 2),
@@ -661,87 +741,6 @@ def cpu_baseline(synth, gemv_seconds=12.0, item_seconds=1.2):
             "sample": f"every (N, M) pair of the GEMV step on the first {frac:.4%} of "
                       f"weight rows ({b} weight bytes)",
             "per_config": per}
-
-
-def oracle_per_config(synth, target_s):
-    """The oracle on each workload's steps other than the headline GEMV,
-    every input built as the GPU rows build it; each step is timed on the
-    first `u` rows of the input its cost scales with (activation rows for
-    the GEMMs), u sized from a probe to take about target_s."""
-    import numpy as np
-    import oracle
-    bits = synth.to_numpy_bits
-    res = {}
-
-    def item(name, unit, full, work, run, what):
-        u = max(1, full // 2048)
-        t0 = time.perf_counter()
-        run(u)
-        t = time.perf_counter() - t0
-        u = int(min(full, max(u, u * target_s / max(t, 1e-4))))
-        t0 = time.perf_counter()
-        run(u)
-        t = time.perf_counter() - t0
-        rate = work(u) / t / 1e9
-        res[name] = {"value": round(rate, 4), "unit": unit, "seconds": round(t, 3),
-                     "sample": f"{what} {u} of {full}"}
-        log(f"cpu oracle {name}: {rate:.4g} {unit} ({what} {u} of {full}, {t:.2f} s)")
-
-    # W4A8 tiny (N=256, K=512, M=16), whole: requant_w + requant_a + GEMM.
-    c = synth.w4a8_tiny("cpu")
-    wp0, we0, a0 = bits(c.w_packed), bits(c.w_e4m3), bits(c.a_bf16)
-
-    def tiny(_):
-        wq, wsc = oracle.requant_w_nvfp4_int8(wp0, we0, c.scale2)
-        aq, asc = oracle.requant_a_bf16_int8(a0)
-        oracle.int8_gemm_blockscaled(aq, wq, asc, wsc)
-    item("w4a8_tiny_step", "GFLOP/s", 1, lambda u: 2 * 16 * 256 * 512, tiny, "whole step,")
-
-    # W4A8 prefill: NVFP4 weight 17408x5120 -> int8; acts 2048x5120.
-    m, n, k = 2048, 17408, 5120
-    c = synth.w4a8_prefill("cpu", m, n, k)
-    wb, ab = bits(c.w_bf16), bits(c.a_bf16)
-    wp, we = oracle.quantize_bf16_nvfp4(wb, c.scale2)
-    wq, wsc = oracle.requant_w_nvfp4_int8(wp, we, c.scale2)
-    aq, asc = oracle.requant_a_bf16_int8(ab)
-    item("requant_a_bf16_int8", "GB/s", m, lambda u: u * k * 2 + u * k + u * (k // 32) * 4,
-         lambda u: oracle.requant_a_bf16_int8(ab[:u]), "activation rows")
-    item("requant_w_nvfp4_int8", "GB/s", n,
-         lambda u: u * (k // 2 + k // 16 + k + (k // 32) * 4),
-         lambda u: oracle.requant_w_nvfp4_int8(wp[:u], we[:u], c.scale2), "weight rows")
-    item("int8_gemm_blockscaled", "GFLOP/s", m, lambda u: 2 * u * n * k,
-         lambda u: oracle.int8_gemm_blockscaled(aq[:u], wq, asc[:u], wsc), "activation rows")
-    del c, wb, ab, wp, we, wq, wsc, aq, asc
-
-    # W4A4 prefill: acts 4096x17408 -> NVFP4; NVFP4 weight 5120x17408.
-    m, n, k = 4096, 5120, 17408
-    c = synth.w4a4_prefill("cpu", m, n, k)
-    ab = bits(c.a_bf16)
-    wp, wsc = oracle.quantize_bf16_nvfp4(bits(c.w_bf16), c.scale_w2)
-    ap, asc = oracle.quantize_bf16_nvfp4(ab[:64], 1.0)
-    item("quantize_bf16_nvfp4", "GB/s", m, lambda u: u * (k * 2 + k // 2 + k // 16),
-         lambda u: oracle.quantize_bf16_nvfp4(ab[:u], 1.0), "activation rows")
-    item("w4a4_gemm", "GFLOP/s", 64, lambda u: 2 * u * n * k,
-         lambda u: oracle.w4a4_gemm(ap[:u], asc[:u], wp, wsc, 1.0, c.scale_w2),
-         "activation rows (of the first 64)")
-    del c, ab, wp, wsc, ap, asc
-
-    # Block-FP8 -> row-wise FP8 requant + GEMM: W 12288x5120, acts 8192x5120.
-    m, n, k = 8192, 12288, 5120
-    c = synth.fp8_block("cpu", m, n, k)
-    w, grid = bits(c.w_block), c.block_grid.numpy()
-    ab = bits(c.a_bf16)
-    item("requant_w_blockfp8_rowwise", "GB/s", n // 128, lambda u: 128 * u * (2 * k + 4),
-         lambda u: oracle.requant_w_blockfp8_rowwise(w[:128 * u], grid[:u]),
-         "128-row weight blocks")
-    wq, wsc = oracle.requant_w_blockfp8_rowwise(w, grid)
-    aq, asc = oracle.quant_rowwise_fp8(ab[:256])
-    item("quant_rowwise_fp8", "GB/s", m, lambda u: u * (3 * k + 4),
-         lambda u: oracle.quant_rowwise_fp8(ab[:u]), "activation rows")
-    item("fp8_gemm_rowscale", "GFLOP/s", 256, lambda u: 2 * u * n * k,
-         lambda u: oracle.fp8_gemm_rowscale(aq[:u], asc[:u], wq, wsc),
-         "activation rows (of the first 256)")
-    return res
 
 
 if __name__ == "__main__":
