@@ -31,22 +31,19 @@
 //    loads 16 bytes (32 elements) of weight row l%4 at byte 16 (l/4) of a
 //    256-byte window, so every load instruction covers 4 rows x 256
 //    contiguous bytes -- the burst HBM serves best -- and the weights need
-//    no LDS transpose.  A lane needs 2 scale bytes per window; with wide
-//    weights the workgroup stages whole 128-byte scale lines (4 windows of
-//    a row) in LDS, with narrow ones each lane loads its 2 bytes.
+//    no LDS transpose.  A lane needs 2 scale bytes per window; the workgroup
+//    stages its rows' scale bytes for two windows at a time in LDS.
 //  * Activations: for each 512-element window, lane l uses 32 elements of
 //    activation row 4g + l%4 (M group g) for every weight row group of the
-//    wave.  With wide weights the four waves of a workgroup stage the window
-//    in LDS once (double-buffered, one barrier per window) instead of each
-//    fetching it from L2.
+//    wave.  The four waves of a workgroup stage the window in LDS once
+//    (double-buffered, one barrier per window) instead of each fetching it
+//    from L2.
 //  * Two register stages are used in turn, so each wave keeps the next two
 //    windows in flight.  Every load is a raw buffer load: a lane whose data
 //    does not exist (rows >= n or >= m, K past the end, a prefetch past the
 //    last window) gets an offset beyond the buffer and reads zero without
 //    touching memory, so no load sits under a branch.
-//  * Work split from N alone: wide weights give each wave its own rows over
-//    all of K; narrow weights split the windows of 8 rows over the four
-//    waves of a workgroup and add the partial sums in a fixed order.  No
+//  * Each wave owns 4 or 8 rows (chosen from N alone) over all of K.  No
 //    summation order depends on M, so every output row is bit-identical to
 //    an M = 1 call on that row.
 #include "qp_device.hpp"
@@ -98,13 +95,10 @@ struct W4Wts {
 
 // Per-lane load offsets at window 0 of one wave (rows row0 .. row0 + 4 RG - 1).
 //   weights: lane l -> row 4 rg + l%4, bytes 16 (l/4) .. of the 256-byte window
-//   scales:  the same row, bytes 2 (l/4), +1 of the 32-byte window
-//   direct activation fragments (K split): row 4 g + l%4, elements
-//            32 (l/4) .. +31 of the 512-element window
 template <int MG, int RG>
 struct W4Src {
     buf_rsrc rw, rs, rx;
-    uint32_t wo[RG], so[RG], xo[MG];
+    uint32_t wo[RG];
     uint32_t kc;            // K index of the lane's chunk within a window
 
     __device__ __forceinline__ void init(const uint16_t *x, const uint8_t *wp, const uint8_t *ws,
@@ -119,39 +113,18 @@ struct W4Src {
         for (int rg = 0; rg < RG; ++rg) {
             uint32_t r = row0 + 4 * rg + lane % 4;
             wo[rg] = r < n ? r * (k / 2) + kc / 2 : W4_OOB;
-            so[rg] = r < n ? r * (k / 16) + kc / 16 : W4_OOB;
-        }
-#pragma unroll
-        for (int g = 0; g < MG; ++g) {
-            uint32_t r = 4 * g + lane % 4;
-            xo[g] = r < m ? (r * k + kc) * 2 : W4_OOB;
         }
     }
-    // Window `win`; lanes whose 32-element chunk lies past K (or every lane,
-    // when ok is false) read zero.  SC: also load the lane's scale bytes.
-    template <bool SC = true>
+    // The packed codes of window `win`; lanes whose 32-element chunk lies
+    // past K (or every lane, when ok is false) read zero.  (Scale bytes are
+    // staged in LDS by the workgroup.)
     __device__ __forceinline__ void load_w(W4Wts<RG> &g, uint32_t win, bool ok, uint32_t k) const
     {
         bool in = ok && win * W4_WIN + kc < k;
-        uint32_t dw = in ? win * W4_WB : W4_OOB, ds = in ? win * W4_SB : W4_OOB;
+        uint32_t dw = in ? win * W4_WB : W4_OOB;
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
             g.w[rg] = __builtin_amdgcn_raw_buffer_load_b128(rw, wo[rg] + dw, 0, W4_NT);
-        if constexpr (SC) {
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
-                g.s[rg] = __builtin_amdgcn_raw_buffer_load_b16(rs, so[rg] + ds, 0, 0);
-        }
-    }
-    __device__ __forceinline__ void load_x(W4Act<MG> &a, uint32_t win, bool ok, uint32_t k) const
-    {
-        bool in = ok && win * W4_WIN + kc < k;
-        uint32_t dx = in ? win * W4_WIN * 2 : W4_OOB;
-#pragma unroll
-        for (int g = 0; g < MG; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a.x[g][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo[g] + dx + 16 * i, 0, 0);
     }
 };
 
@@ -392,9 +365,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
     u32x4 xa[XC], xb[XC];
     u32x2 sg[SCH];
     load_sg(sg, 0);
-    src.template load_w<false>(A, 0, nwin > 0, k);
+    src.load_w(A, 0, nwin > 0, k);
     load_xs(xa, 0, nwin > 0);
-    src.template load_w<false>(B, 1, nwin > 1, k);
+    src.load_w(B, 1, nwin > 1, k);
     load_xs(xb, 1, nwin > 1);
     W4Act<MG> frag;
 
@@ -409,7 +382,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
         read_frags(frag, buf);
         read_scales(W, sb, wig);
         w4_window<MG, RG>(acc, W, frag);
-        src.template load_w<false>(W, w + 2, w + 2 < nwin, k);
+        src.load_w(W, w + 2, w + 2 < nwin, k);
     };
     uint32_t win = 0;
     for (; win + 2 <= nwin; win += 2) {
@@ -428,77 +401,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
     w4_store<MG, RG>(acc, scale2, out, row0, m, n, lane);
 }
 
-// ---------------------------------------------------------------------------
-// Narrow weights: the four waves of a workgroup share 4 RG rows and split the
-// K windows; each fetches its own activation fragments, and the partial
-// sums are added in a fixed order.
-// ---------------------------------------------------------------------------
-template <int MG, int RG>
-__global__ __launch_bounds__(256) void k_w4a16_gemv_ksplit(
-    const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
-    const uint8_t *__restrict__ ws, float scale2, uint16_t *__restrict__ out,
-    uint32_t m, uint32_t n, uint32_t k)
-{
-    constexpr int ROWS = 4 * RG;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t row0 = blockIdx.x * ROWS;
-    const uint32_t nwin = (k + W4_WIN - 1) / W4_WIN;
-    const uint32_t w_beg = nwin * wave / 4, w_end = nwin * (wave + 1) / 4;
-
-    W4Src<MG, RG> src;
-    src.init(x, wp, ws, row0, m, n, k, lane);
-
-    f32x4 acc[RG][MG];
-    w4_zero<MG, RG>(acc);
-
-    W4Wts<RG> A, B;
-    W4Act<MG> XA, XB;
-    src.load_w(A, w_beg, w_beg < w_end, k);
-    src.load_x(XA, w_beg, w_beg < w_end, k);
-    src.load_w(B, w_beg + 1, w_beg + 1 < w_end, k);
-    src.load_x(XB, w_beg + 1, w_beg + 1 < w_end, k);
-    uint32_t win = w_beg;
-    for (; win + 2 <= w_end; win += 2) {
-        w4_window<MG, RG>(acc, A, XA);
-        src.load_w(A, win + 2, win + 2 < w_end, k);
-        src.load_x(XA, win + 2, win + 2 < w_end, k);
-        w4_window<MG, RG>(acc, B, XB);
-        src.load_w(B, win + 3, win + 3 < w_end, k);
-        src.load_x(XB, win + 3, win + 3 < w_end, k);
-    }
-    if (win < w_end)                // an odd last window, already in A
-        w4_window<MG, RG>(acc, A, XA);
-
-    w4_block_sum<MG, RG>(acc);
-
-    // Fixed-order sum of the four K parts of each row group.
-    __shared__ f32x4 red[4][RG][MG][4];
-    if (lane < 4) {
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int g = 0; g < MG; ++g)
-                red[wave][rg][g][lane] = acc[rg][g];
-    }
-    __syncthreads();
-    if (wave != 0)
-        return;
-    if (lane < 4) {
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int g = 0; g < MG; ++g)
-                acc[rg][g] = ((red[0][rg][g][lane] + red[1][rg][g][lane]) + red[2][rg][g][lane]) +
-                             red[3][rg][g][lane];
-    }
-    w4_store<MG, RG>(acc, scale2, out, row0, m, n, lane);
-}
-
-// Row groups per wave (8 weight rows) for one and two M groups: more rows
-// per wave cost registers faster than they save activation reads.
-constexpr int W4_RG1 = 2, W4_RG2 = 2;
-
-// Work-split choice from n alone (never m).
+// Row groups per wave, from n alone (never m): two (8 weight rows) for wide
+// weights; one (4 rows) for narrow ones, so that they still spread over all
+// CUs (N = 6144: 384 workgroups of 16 rows).  Measured at K = 5120 against the
+// earlier K-split kernel for narrow weights (four waves sharing 8 rows, each
+// a quarter of K): N = 17408, M = 1 / 2 / 8: 17.4 / 18.6 / 36.5 -> 12.5 /
+// 12.9 / 18.8 us; N = 6144: 8.3 / 8.9 / 15.2 -> 7.4 / 7.5 / 9.2 us.
 static bool w4_gemv_wide(uint32_t n) { return n >= 65536u; }
 
 template <int MG, int RG>
@@ -506,15 +414,9 @@ static void launch_w4(const uint16_t *x, const uint8_t *wp, const uint8_t *ws, f
                       uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t st)
 {
     constexpr uint32_t ROWS = 4 * RG;
-    if (w4_gemv_wide(n)) {
-        uint32_t grid = (n + 4 * ROWS - 1) / (4 * ROWS);
-        hipLaunchKernelGGL((k_w4a16_gemv_rows<MG, RG>), dim3(grid), dim3(256), 0, st,
-                           x, wp, ws, scale2, out, m, n, k);
-    } else {
-        uint32_t grid = (n + ROWS - 1) / ROWS;
-        hipLaunchKernelGGL((k_w4a16_gemv_ksplit<MG, RG>), dim3(grid), dim3(256), 0, st,
-                           x, wp, ws, scale2, out, m, n, k);
-    }
+    const uint32_t grid = (n + 4 * ROWS - 1) / (4 * ROWS);
+    hipLaunchKernelGGL((k_w4a16_gemv_rows<MG, RG>), dim3(grid), dim3(256), 0, st,
+                       x, wp, ws, scale2, out, m, n, k);
 }
 
 // 1 <= m <= 8, k % 32 == 0 and every buffer < 2^30 bytes (checked by the
@@ -523,10 +425,13 @@ hipError_t launch_w4a16_gemv(const uint16_t *x, const uint8_t *wp, const uint8_t
                              float scale2, uint16_t *out, uint32_t m, uint32_t n,
                              uint32_t k, hipStream_t st)
 {
+    const bool wide = w4_gemv_wide(n);
     if (m <= 4)
-        launch_w4<1, W4_RG1>(x, wp, ws, scale2, out, m, n, k, st);
+        wide ? launch_w4<1, 2>(x, wp, ws, scale2, out, m, n, k, st)
+             : launch_w4<1, 1>(x, wp, ws, scale2, out, m, n, k, st);
     else
-        launch_w4<2, W4_RG2>(x, wp, ws, scale2, out, m, n, k, st);
+        wide ? launch_w4<2, 2>(x, wp, ws, scale2, out, m, n, k, st)
+             : launch_w4<2, 1>(x, wp, ws, scale2, out, m, n, k, st);
     count_launch();
     return hipGetLastError();
 }
