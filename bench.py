@@ -61,8 +61,9 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true", help="GEMV step only")
     ap.add_argument("--only", default="", help="comma list of secondary items to run")
     ap.add_argument("--skip-gemv", action="store_true",
-                    help="run only the secondary rows (for profiling them); prints "
-                         "their JSON dictionary instead of the headline line")
+                    help="run only the secondary rows (for profiling them), after one "
+                         "1 GiB copy (counter calibration); prints their JSON "
+                         "dictionary instead of the headline line")
     ap.add_argument("--roofline-only", action="store_true",
                     help="for hardware-counter runs: one plain 1 GiB copy (counter "
                          "calibration), then the lm_head GEMV at each M, 5 launches each")
@@ -163,6 +164,7 @@ def main():
         return
     if args.skip_gemv:
         only = set(s for s in args.only.split(",") if s)
+        calibration_copy(torch, dev)
         print(json.dumps({"secondary": run_secondary(qp, synth, dev, only)}), flush=True)
         return
 
@@ -288,17 +290,24 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def calibration_copy(torch, dev):
+    """One device-to-device copy of exactly 1 GiB: it reads 1 GiB and writes
+    1 GiB, which scales FETCH_SIZE / WRITE_SIZE to bytes in a counter run."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def roofline_only(qp, synth, dev):
     """A short program for counter runs: a device-to-device copy of exactly
     1 GiB (reads 1 GiB, writes 1 GiB: the scale for FETCH_SIZE / WRITE_SIZE),
     then 5 launches of the lm_head GEMV at each M, each on a fresh weight copy
     (two copies of 778 MB, so nothing stays cache-resident)."""
     import torch
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
+    calibration_copy(torch, dev)
     n, k = 152064, 5120
     wb = synth.gemv_weight_bf16(n, k, dev, shape_id=2)
     wq = torch.empty((n, k), dtype=torch.uint8, device=dev)

@@ -126,7 +126,10 @@ __global__ __launch_bounds__(256) void k_fp8_gemm_rowscale(
 // The MFMAs compute C^T tiles (W fragment as the first operand): lane l then
 // holds row l % 32 of C and, in accumulator registers 4q .. 4q+3, four
 // consecutive columns 8q + 4*(l/32) .. +3, so the epilogue scales and
-// converts four outputs at a time and writes them with one 8-byte store.
+// converts four outputs at a time.  Written straight from that layout, each
+// store instruction would touch 32 rows (32 cache lines, 16 bytes each);
+// instead every wave stages its 128 x 128 BF16 block in a free LDS slot and
+// stores it row by row, 4 rows of 256 bytes per instruction.
 // The MFMA is issued with zero scale operands, which selects the unscaled
 // encoding (identical results to unit E8M0 scales, at lower power).
 // ---------------------------------------------------------------------------
@@ -230,15 +233,17 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
                     f.w[i % 4], f.a[i / 4], acc[i / 4][i % 4], 0, 0, 0, 0, 0, 0);
     };
     auto interleave = [&](int n_mfma, int n_ds, int n_vmem) {
-        // n_ds LDS reads and n_vmem DMA loads, two after each of the first
-        // MFMAs (reads early, so they have returned by the time their
-        // fragments are needed)
+        // n_ds LDS reads, two after each of the first MFMAs (early, so they
+        // have returned by the time their fragments are needed), and n_vmem
+        // DMA loads, one after each of the first MFMAs: the DMA of a stage
+        // is spread over its 16 MFMAs so that the address unit never holds
+        // a burst of them (issued two per MFMA the kernel ran 6% slower)
         for (int i = 0; i < n_mfma; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (2 * i < n_ds)
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            if (2 * i < n_vmem)
-                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            if (i < n_vmem)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
     // Wait until at most n of this wave's loads are in flight and its LDS
@@ -254,31 +259,28 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
     // Stage st, X = (st, K step 0) already in registers, A(st) and W(st) in
     // slots ca and cw, A(st+1) and W(st+1) due in na and nw:
     //   16 MFMAs on X + LDS reads of Y = (st, K step 1)
-    //    4 MFMAs on Y
     //   sync: A(st+1) and W(st+1) have landed (only A(st+2) may still be
     //         in flight: 8 loads per wave), and every wave has finished
     //         reading ca and cw
     //   DMA of W(st+2) into ca and A(st+3) into cw
-    //   12 MFMAs on Y + LDS reads of X = (st+1, K step 0) and the DMA,
-    //      all issued over the first 8, so the reads have returned before
-    //      the next stage needs them
+    //   16 MFMAs on Y + LDS reads of X = (st+1, K step 0), issued over the
+    //      first 8 so that they have returned before the next stage needs
+    //      them, and the 16 DMA loads, one per MFMA
     // The slots are passed as the LDS variables themselves so that every
     // access names its slot statically.
     Frags X, Y;
-    constexpr int Y_PRE = 4;      // MFMAs on Y before the sync
     auto stage = [&](uint32_t st, uint8_t *ca, uint8_t *cw, const uint8_t *na,
                      const uint8_t *nw) {
         launder();
         read_frags(Y, ca, cw, 1);
         mfma_range(X, 0, 16);
         interleave(16, 16, 0);
-        mfma_range(Y, 0, Y_PRE);
         sync_stage(std::integral_constant<int, 8>());
         dma_panel(w_rows, st + 2, ca);
         dma_panel(a_rows, st + 3, cw);
         read_frags(X, na, nw, 0);
-        mfma_range(Y, Y_PRE, 16);
-        interleave(16 - Y_PRE, 16, 16);
+        mfma_range(Y, 0, 16);
+        interleave(16, 16, 16);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
 
     // Epilogue: C[i][j] = bf16(acc * (as[i] * ws[j])).  Lane rows
     // i = ib + 32*ti, columns j = jb + 32*tj + 8*q + c (c = 0..3); a shifted
-    // tile stores only rows >= m0 and columns >= n0.
+    // tile stores only rows >= m0 and columns >= n0, element by element.
     const uint32_t ib = m0e + wm * 128 + (lane & 31);
     const uint32_t jb = n0e + wn * 128 + 4 * (lane >> 5);
     if (vec_ok && m0e == m0 && n0e == n0) {
@@ -332,9 +334,16 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 sw[tj][q] = *reinterpret_cast<const f32x4 *>(ws + jb + 32 * tj + 8 * q);
+        // Stage the wave's 128 x 128 block in slot `wave` (every wave has
+        // finished reading the slots and its DMA has landed), 256 bytes per
+        // row.  8-byte unit u of row r sits at u ^ (r % 32): the 32 lanes of
+        // a half-wave (rows r % 32 = 0..31, one unit each) then write 32
+        // different units of their rows, all 64 banks.
+        __syncthreads();
+        uint8_t *const ep = wave == 0 ? S0 : wave == 1 ? S1 : wave == 2 ? S2 : S3;
+        const int r5 = lane & 31, hh = lane >> 5;
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-            uint16_t *orow = out + (size_t)(ib + 32 * ti) * N + jb;
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
@@ -345,8 +354,22 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
                                     c[4 * q + 1] * (sa[ti] * sw[tj][q][1]));
                     pk[1] = pk_bf16(c[4 * q + 2] * (sa[ti] * sw[tj][q][2]),
                                     c[4 * q + 3] * (sa[ti] * sw[tj][q][3]));
-                    *reinterpret_cast<u32x2 *>(orow + 32 * tj + 8 * q) = pk;
+                    *reinterpret_cast<u32x2 *>(ep + (r5 + 32 * ti) * 256 + 8 * ((8 * tj + 2 * q + hh) ^ r5)) = pk;
                 }
+        }
+        // Read back 16-byte units p (physical) of 4 rows per instruction:
+        // they hold logical units p ^ ((r % 32) >> 1), with their two
+        // 8-byte halves swapped in odd rows.
+        const int p = lane & 15;
+        uint16_t *const obase = out + (size_t)(m0 + wm * 128) * N + n0 + wn * 128;
+#pragma unroll 4
+        for (int it = 0; it < 32; ++it) {
+            const int r = 4 * it + (lane >> 4);
+            u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * 256 + 16 * p);
+            if (r & 1)
+                v = (u32x4){v[2], v[3], v[0], v[1]};
+            const int lc = p ^ ((r & 31) >> 1);
+            *reinterpret_cast<u32x4 *>(obase + (size_t)r * N + 8 * lc) = v;
         }
     } else {
 #pragma unroll
@@ -373,10 +396,10 @@ hipError_t launch_fp8_gemm_rowscale(const uint8_t *a, const float *as,
 {
     if (k % BIG_KB == 0 && m >= 256 && n >= 256) {
         uint32_t mt = (m + 255) / 256, nt = (n + 255) / 256;
-        // 8-byte output stores and 16-byte column-scale loads need N % 4 == 0
-        // and aligned base pointers; otherwise every tile takes the
-        // element-wise epilogue.
-        uint32_t vec_ok = n % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0 &&
+        // 16-byte output stores and column-scale loads need N % 8 == 0 and
+        // aligned base pointers; otherwise every tile takes the element-wise
+        // epilogue.
+        uint32_t vec_ok = n % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0 &&
                           reinterpret_cast<uintptr_t>(ws) % 16 == 0;
         hipLaunchKernelGGL(k_fp8_gemm_rowscale_big, dim3(mt * nt), dim3(256), 0, st,
                            a, as, w, ws, out, m, n, k, mt, nt, vec_ok);
