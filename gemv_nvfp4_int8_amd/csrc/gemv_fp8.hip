@@ -303,13 +303,15 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     const float *__restrict__ rs, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k)
 {
-    static_assert(R == 8 || R == 16, "8 or 16 rows per workgroup");
+    static_assert(R == 8 || R == 16 || R == 32, "8, 16 or 32 rows per workgroup");
     static_assert(XP == 1 || XP == 2 || XP == 4 || XP == 8, "1, 2, 4 or 8 row pairs");
+    // MFMA weight tiles of 16 rows (R = 8: one, its rows 8..15 zero)
+    constexpr int NT = R < 16 ? 1 : R / 16;
     // per wave: R weight rows + a zero row; 2 XP activation rows + a zero row
-    constexpr int WROWS = R < 16 ? R + 1 : 16, XROWS = XP < 8 ? 2 * XP + 1 : 16;
+    constexpr int WROWS = R < 16 ? R + 1 : R, XROWS = XP < 8 ? 2 * XP + 1 : 16;
     __shared__ __attribute__((aligned(16))) uint8_t sw[4][WROWS * GV_WPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t sx[4][XROWS * GV_XPITCH];
-    __shared__ f32x4 red[3][WAVE];
+    __shared__ f32x4 red[3][NT][WAVE];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -379,14 +381,20 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     if constexpr (XP < 8)
         if (lane < GV_XPITCH / 8)
             *reinterpret_cast<u32x4 *>(&sx[wave][2 * XP * GV_XPITCH + 8 * lane]) = (u32x4){0, 0, 0, 0};
-    // the LDS rows this lane's MFMA operands come from
+    // the LDS rows this lane's MFMA operands come from (weight tile t: row
+    // wrow + 16 t)
     const int wrow = R < 16 && col >= R ? R : col;
     const int xrow = XP < 8 && col >= 2 * XP ? 2 * XP : col;
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NT];
     // BS: the last block partial not yet folded, and its scale (a zero
     // partial with scale 0 before the first segment)
-    f32x4 p_pend = {0.f, 0.f, 0.f, 0.f};
+    f32x4 p_pend[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        p_pend[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
     float s_pend = 0.f;
 
     // D stages in flight.  The loop is unrolled by D so every stage is a
@@ -410,61 +418,75 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         const float s_lo = g[d].s[0];
         const float s_hi = g[d].s[1];
         load(g[d], seg + D);
-        f32x4 p[2];         // partials of the segment's two K blocks (BS)
+        f32x4 p[2][NT];     // partials of the segment's two K blocks (BS)
 #pragma unroll
         for (int u = 0; u < GV_SEG / 64; ++u) {
             const uint16_t *xp = &sx[wave][xrow * GV_XPITCH + 64 * u + 16 * grp];
             const u32x4 xa = *reinterpret_cast<const u32x4 *>(xp);
             const u32x4 xb = *reinterpret_cast<const u32x4 *>(xp + 8);
-            const u32x4 wv = *reinterpret_cast<const u32x4 *>(
-                &sw[wave][wrow * GV_WPITCH + 64 * u + 16 * grp]);
-            bf16x8 blo, bhi;
-            fp8x16_to_bf16(wv, blo, bhi);
-            if constexpr (BS) {
-                f32x4 &pb = p[u / 2];
-                if (u % 2 == 0)
-                    pb = (f32x4){0.f, 0.f, 0.f, 0.f};
-                pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, pb, 0, 0, 0);
-                pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, pb, 0, 0, 0);
-                // Folds trail the MFMAs that produce them by one K step, so
-                // the MFMA results are not waited for: the previous
-                // segment's second block after this segment's first step,
-                // this segment's first block after its third step.  The
-                // order of the additions is still block by block along K.
-                if (u == 0)
-                    fold_block(acc, s_pend, p_pend);
-                if (u == 2)
-                    fold_block(acc, s_lo, p[0]);
-            } else {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const u32x4 wv = *reinterpret_cast<const u32x4 *>(
+                    &sw[wave][(wrow + 16 * t) * GV_WPITCH + 64 * u + 16 * grp]);
+                bf16x8 blo, bhi;
+                fp8x16_to_bf16(wv, blo, bhi);
+                if constexpr (BS) {
+                    f32x4 &pb = p[u / 2][t];
+                    if (u % 2 == 0)
+                        pb = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, pb, 0, 0, 0);
+                    pb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, pb, 0, 0, 0);
+                    // Folds trail the MFMAs that produce them by one K step,
+                    // so the MFMA results are not waited for: the previous
+                    // segment's second block after this segment's first
+                    // step, this segment's first block after its third step.
+                    // The order of the additions is still block by block
+                    // along K.
+                    if (u == 0)
+                        fold_block(acc[t], s_pend, p_pend[t]);
+                    if (u == 2)
+                        fold_block(acc[t], s_lo, p[0][t]);
+                } else {
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
+                }
             }
         }
         if constexpr (BS) {
-            p_pend = p[1];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                p_pend[t] = p[1][t];
             s_pend = s_hi;
         }
     }
     if constexpr (BS)
-        fold_block(acc, s_pend, p_pend);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            fold_block(acc[t], s_pend, p_pend[t]);
 
     // Fixed-order reduction of the four K-quarter partial tiles.
     if (wave > 0)
-        red[wave - 1][lane] = acc;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            red[wave - 1][t][lane] = acc[t];
     __syncthreads();
     if (wave != 0)
         return;
 #pragma unroll
-    for (int v = 0; v < 3; ++v)
-        acc += red[v][lane];
-    const uint32_t nn = row0 + col;
-    if (col < R && nn < n) {
-        const float sc = BS ? 1.0f : rs[nn];
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t mm = 4u * grp + i;
-            if (mm < m)
-                out[(size_t)mm * n + nn] = (uint16_t)f32_to_bf16(BS ? acc[i] : acc[i] * sc);
+        for (int v = 0; v < 3; ++v)
+            acc[t] += red[v][t][lane];
+        const uint32_t nn = row0 + 16 * t + col;
+        if (col < R && nn < n) {
+            const float sc = BS ? 1.0f : rs[nn];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t mm = 4u * grp + i;
+                if (mm < m)
+                    out[(size_t)mm * n + nn] =
+                        (uint16_t)f32_to_bf16(BS ? acc[t][i] : acc[t][i] * sc);
+            }
         }
     }
 }
@@ -472,9 +494,16 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 // Rows per workgroup and activation row pairs follow M: at M <= 2 the
 // 8-row unit spreads the weight evenly over the CUs; from M = 3 on, the
 // activation rows every workgroup loads outweigh the balance, and 16 rows
-// halve them (measured on N = 6144 and 17408).  Neither choice changes any
-// row's summation order.
-template <int D, bool BS>
+// halve them (measured on N = 6144 and 17408).  Above M = 8 the activation
+// bytes a workgroup reads are twice its weight bytes at 16 rows, and R16
+// rows per workgroup (32 where the grid stays at two or more workgroups per
+// CU) halve them again: N = 17408, M = 16 measured 27.5 -> 26.7 us, while
+// at M = 8 the 32-row grid loses more to its uneven last round than it
+// saves.  (Loading the activations straight into MFMA operand registers
+// instead of through LDS was slower at every M > 2: each load instruction
+// then touches 16 rows.)  None of these choices changes any row's
+// summation order.
+template <int D, bool BS, int R16>
 static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float *rs,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                                hipStream_t st)
@@ -489,7 +518,7 @@ static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float 
     else if (m <= 8)
         QP_GEMV_KSPLIT(16, 4);
     else
-        QP_GEMV_KSPLIT(16, 8);
+        QP_GEMV_KSPLIT(R16, 8);
 #undef QP_GEMV_KSPLIT
 }
 
@@ -512,16 +541,17 @@ static bool gemv_wide(uint32_t n) { return n >= 65536u; }
 
 // Segments in flight per wave for the K-split kernel: two once the grid has
 // several workgroups per CU (measured: N = 17408 gains 4-5% at every M,
-// N = 6144 loses 0-3%).  The depth changes no summation order.
+// N = 6144 loses 0-3%), together with 32-row workgroups above M = 8.  The
+// depth changes no summation order.
 template <bool BS>
 static void launch_gemv_narrow(const uint16_t *x, const uint8_t *w, const float *rs,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                                hipStream_t st)
 {
     if (n >= 12288u)
-        launch_gemv_ksplit<2, BS>(x, w, rs, out, m, n, k, st);
+        launch_gemv_ksplit<2, BS, 32>(x, w, rs, out, m, n, k, st);
     else
-        launch_gemv_ksplit<1, BS>(x, w, rs, out, m, n, k, st);
+        launch_gemv_ksplit<1, BS, 16>(x, w, rs, out, m, n, k, st);
 }
 
 hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
