@@ -271,17 +271,18 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 
 // ---------------------------------------------------------------------------
 // Narrow weights: too few rows to give every CU several workgroups, so the
-// four waves of a workgroup share R rows (8 or 16) and split K into
-// contiguous quarters.  Everything is wave-private (the weight transpose tile
-// and the activation segment live in the wave's own LDS region, so the loop
-// has no barrier), D segments are loaded ahead, and the four partial tiles
-// are added in a fixed order at the end.
+// four waves of a workgroup share R rows (8, 16 or 32) and split K into
+// contiguous quarters (ending on 256-element boundaries).  Everything is
+// wave-private (the weight transpose tile and the activation segment live in
+// the wave's own LDS region, so the loop has no barrier), D segments of SEG
+// K elements are loaded ahead, and the four partial tiles are added in a
+// fixed order at the end.
 //
 // R = 8 halves the work unit so that narrow weights spread evenly over the
 // CUs (N = 6144: 768 workgroups, three per CU, against 384 of 16 rows); the
-// MFMA's weight rows 8..15 then read an all-zero LDS row.  XP is the number
-// of activation row pairs loaded per segment (M <= 2 XP); the rows past them
-// likewise read a zero row.  Neither changes any summation order.
+// MFMA's weight rows 8..15 then read an all-zero LDS row.  XR activation
+// rows are loaded per segment (M <= XR); the rows past them likewise read a
+// zero row.  None of R, XR, D and SEG changes any summation order.
 //
 // Every load is a raw buffer load from a 32-bit offset (n*k < 2^31,
 // m*k < 2^31).  Rows past N, bytes past K, activation rows past M and
@@ -290,34 +291,43 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 // branch, so the compiler counts the loads in flight exactly and waits only
 // for the stage it is about to use.
 // ---------------------------------------------------------------------------
-template <int R, int XP>
+template <int R, int NW, int NX>
 struct GvSegK {
-    u32x4 w[R / 4];      // R rows x 256 B, 4 rows per instruction
-    u32x4 x[XP];         // 2 XP rows x 256 bf16, 16 B per lane and row pair
+    u32x4 w[NW];         // R weight rows of the segment, 1 KB per instruction
+    u32x4 x[NX];         // XR activation rows of the segment, 1 KB per instruction
     float s[2];          // block scales of the segment's two K blocks (BS)
 };
 
-template <int R, int XP, int D, bool BS>
+template <int R, int XR, int D, bool BS, int SEG>
 __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
     const float *__restrict__ rs, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k)
 {
     static_assert(R == 8 || R == 16 || R == 32, "8, 16 or 32 rows per workgroup");
-    static_assert(XP == 1 || XP == 2 || XP == 4 || XP == 8, "1, 2, 4 or 8 row pairs");
+    static_assert(XR == 2 || XR == 4 || XR == 8 || XR == 16, "2, 4, 8 or 16 activation rows");
+    static_assert(SEG == 256 || (SEG == 128 && !BS), "256-element segments, or 128 without block scales");
     // MFMA weight tiles of 16 rows (R = 8: one, its rows 8..15 zero)
     constexpr int NT = R < 16 ? 1 : R / 16;
-    // per wave: R weight rows + a zero row; 2 XP activation rows + a zero row
-    constexpr int WROWS = R < 16 ? R + 1 : R, XROWS = XP < 8 ? 2 * XP + 1 : 16;
-    __shared__ __attribute__((aligned(16))) uint8_t sw[4][WROWS * GV_WPITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t sx[4][XROWS * GV_XPITCH];
+    // 16-byte chunks per weight row and 8-element chunks per activation row
+    // of a segment; rows one load instruction covers
+    constexpr int WCH = SEG / 16, XCH = SEG / 8;
+    constexpr int WRPI = 64 / WCH, XRPI = 64 / XCH;
+    constexpr int NW = R / WRPI, NX = (XR + XRPI - 1) / XRPI;
+    constexpr int WPITCH = SEG + 16, XPITCH = SEG + 8;
+    // per wave: R weight rows + a zero row; XR activation rows + a zero row
+    constexpr int WROWS = R < 16 ? R + 1 : R, XROWS = XR < 16 ? XR + 1 : 16;
+    __shared__ __attribute__((aligned(16))) uint8_t sw[4][WROWS * WPITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sx[4][XROWS * XPITCH];
     __shared__ f32x4 red[3][NT][WAVE];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const uint32_t row0 = blockIdx.x * R;
-    const uint32_t nseg = (k + GV_SEG - 1) / GV_SEG;
-    const uint32_t per = (nseg + 3) / 4;
+    // K quarters end on 256-element boundaries whatever SEG is, so that a
+    // row's summation order never depends on the launch shape.
+    const uint32_t per = ((k + 255) / 256 + 3) / 4 * (256 / SEG);
+    const uint32_t nseg = (k + SEG - 1) / SEG;
     const uint32_t s_beg = min(nseg, per * wave), s_end = min(nseg, s_beg + per);
     const uint32_t kbl = k / 128;
 
@@ -328,63 +338,72 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         (void *)rs, 0, BS ? 4 * (n / 128) * kbl : 4 * n, 0x00020000);
     const uint32_t sbase = BS ? 4 * (row0 / 128) * kbl : 0;
 
-    // weight instruction j: row 4j + grp, bytes 16 col .. +15 of the segment
-    uint32_t wofs[R / 4];
+    // weight instruction j: row WRPI j + lane / WCH, bytes 16 (lane % WCH)
+    // .. +15 of the segment
+    const int wc = lane % WCH, wr0 = lane / WCH;
+    uint32_t wofs[NW];
 #pragma unroll
-    for (int j = 0; j < R / 4; ++j) {
-        const uint32_t r = row0 + 4 * j + grp;
-        wofs[j] = r < n ? r * k + 16 * col : OOB;
+    for (int j = 0; j < NW; ++j) {
+        const uint32_t r = row0 + WRPI * j + wr0;
+        wofs[j] = r < n ? r * k + 16 * wc : OOB;
     }
-    // activation chunk c = lane + 64 i: row c / 32, elements 8 (c % 32) .. +7
-    uint32_t xofs[XP];
+    // activation instruction i: row XRPI i + lane / XCH, elements
+    // 8 (lane % XCH) .. +7 of the segment
+    const int xc = lane % XCH, xr0 = lane / XCH;
+    uint32_t xofs[NX];
 #pragma unroll
-    for (int i = 0; i < XP; ++i) {
-        const int c = lane + 64 * i, r = c >> 5;
-        xofs[i] = (uint32_t)r < m ? 2 * ((uint32_t)r * k + 8 * (c & 31)) : OOB;
+    for (int i = 0; i < NX; ++i) {
+        const uint32_t r = XRPI * i + xr0;
+        xofs[i] = r < m ? 2 * (r * k + 8 * xc) : OOB;
     }
 
-    auto load = [&](GvSegK<R, XP> &g, uint32_t seg) {
+    auto load = [&](GvSegK<R, NW, NX> &g, uint32_t seg) {
         const bool live = seg < s_end;
-        const uint32_t kb = seg * GV_SEG;
+        const uint32_t kb = seg * SEG;
         if constexpr (BS) {
             g.s[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                 sr, live ? sbase + 8 * seg : OOB, 0, 0));
             g.s[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                 sr, live && 2 * seg + 1 < kbl ? sbase + 8 * seg + 4 : OOB, 0, 0));
         }
-        const bool wlive = live && kb + 16 * col < k;
+        const bool wlive = live && kb + 16 * wc < k;
 #pragma unroll
-        for (int j = 0; j < R / 4; ++j)
+        for (int j = 0; j < NW; ++j)
             g.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                 wr, wlive ? wofs[j] + kb : OOB, 0, 2));
+        const bool xlive = live && kb + 8 * xc < k;
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int c = lane + 64 * i;
+        for (int i = 0; i < NX; ++i)
             g.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                xr, live && kb + 8 * (c & 31) < k ? xofs[i] + 2 * kb : OOB, 0, 0));
-        }
+                xr, xlive ? xofs[i] + 2 * kb : OOB, 0, 0));
     };
-    auto stash = [&](const GvSegK<R, XP> &g) {
+    auto stash = [&](const GvSegK<R, NW, NX> &g) {
 #pragma unroll
-        for (int j = 0; j < R / 4; ++j)
-            *reinterpret_cast<u32x4 *>(&sw[wave][(4 * j + grp) * GV_WPITCH + 16 * col]) = g.w[j];
+        for (int j = 0; j < NW; ++j)
+            *reinterpret_cast<u32x4 *>(&sw[wave][(WRPI * j + wr0) * WPITCH + 16 * wc]) = g.w[j];
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int c = lane + 64 * i;
-            *reinterpret_cast<u32x4 *>(&sx[wave][(c >> 5) * GV_XPITCH + 8 * (c & 31)]) = g.x[i];
-        }
+        for (int i = 0; i < NX; ++i)
+            if (XRPI * (i + 1) <= XROWS || XRPI * i + xr0 < XROWS)
+                *reinterpret_cast<u32x4 *>(&sx[wave][(XRPI * i + xr0) * XPITCH + 8 * xc]) = g.x[i];
     };
+    // The lanes of a wave exchange data through its LDS region with no
+    // barrier (a wave's LDS operations execute in order).  The compiler
+    // does not know that other lanes wrote what a lane reads, so a
+    // wavefront-scope fence (no instruction) separates each stash from the
+    // reads around it: without it, where a lane skips a stash store the
+    // compiler may reuse that lane's previous read of the same address.
+    auto wave_fence = [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); };
     // the zero rows (written once; stash never touches them)
     if constexpr (R < 16)
-        if (lane < GV_WPITCH / 16)
-            *reinterpret_cast<u32x4 *>(&sw[wave][R * GV_WPITCH + 16 * lane]) = (u32x4){0, 0, 0, 0};
-    if constexpr (XP < 8)
-        if (lane < GV_XPITCH / 8)
-            *reinterpret_cast<u32x4 *>(&sx[wave][2 * XP * GV_XPITCH + 8 * lane]) = (u32x4){0, 0, 0, 0};
+        if (lane < WPITCH / 16)
+            *reinterpret_cast<u32x4 *>(&sw[wave][R * WPITCH + 16 * lane]) = (u32x4){0, 0, 0, 0};
+    if constexpr (XR < 16)
+        if (lane < XPITCH / 8)
+            *reinterpret_cast<u32x4 *>(&sx[wave][XR * XPITCH + 8 * lane]) = (u32x4){0, 0, 0, 0};
     // the LDS rows this lane's MFMA operands come from (weight tile t: row
     // wrow + 16 t)
     const int wrow = R < 16 && col >= R ? R : col;
-    const int xrow = XP < 8 && col >= 2 * XP ? 2 * XP : col;
+    const int xrow = XR < 16 && col >= XR ? XR : col;
 
     f32x4 acc[NT];
     // BS: the last block partial not yet folded, and its scale (a zero
@@ -400,7 +419,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     // D stages in flight.  The loop is unrolled by D so every stage is a
     // statically named variable: stage d holds segment seg + d, and is
     // reloaded with segment seg + d + D as soon as it has been stashed.
-    GvSegK<R, XP> g[D];
+    GvSegK<R, NW, NX> g[D];
 #pragma unroll
     for (int d = 0; d < D; ++d)
         load(g[d], s_beg + d);
@@ -411,7 +430,9 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         const uint32_t seg = seg0 + d;
         if (seg >= s_end)
             break;
+        wave_fence();
         stash(g[d]);
+        wave_fence();
         // The second block of a segment may lie past K (K an odd number of
         // 128-blocks); its scale then reads zero and its zero partial adds
         // nothing.
@@ -420,14 +441,14 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         load(g[d], seg + D);
         f32x4 p[2][NT];     // partials of the segment's two K blocks (BS)
 #pragma unroll
-        for (int u = 0; u < GV_SEG / 64; ++u) {
-            const uint16_t *xp = &sx[wave][xrow * GV_XPITCH + 64 * u + 16 * grp];
+        for (int u = 0; u < SEG / 64; ++u) {
+            const uint16_t *xp = &sx[wave][xrow * XPITCH + 64 * u + 16 * grp];
             const u32x4 xa = *reinterpret_cast<const u32x4 *>(xp);
             const u32x4 xb = *reinterpret_cast<const u32x4 *>(xp + 8);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const u32x4 wv = *reinterpret_cast<const u32x4 *>(
-                    &sw[wave][(wrow + 16 * t) * GV_WPITCH + 64 * u + 16 * grp]);
+                    &sw[wave][(wrow + 16 * t) * WPITCH + 64 * u + 16 * grp]);
                 bf16x8 blo, bhi;
                 fp8x16_to_bf16(wv, blo, bhi);
                 if constexpr (BS) {
@@ -503,22 +524,22 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 // instead of through LDS was slower at every M > 2: each load instruction
 // then touches 16 rows.)  None of these choices changes any row's
 // summation order.
-template <int D, bool BS, int R16>
+template <int D, bool BS, int R16, int SEG_SMALL, int SEG_BIG>
 static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float *rs,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                                hipStream_t st)
 {
-#define QP_GEMV_KSPLIT(R, XP)                                                             \
-    hipLaunchKernelGGL((k_fp8_gemv_ksplit<R, XP, D, BS>), dim3((n + R - 1) / R), dim3(256), \
-                       0, st, x, w, rs, out, m, n, k)
+#define QP_GEMV_KSPLIT(R, XR, SEG)                                                          \
+    hipLaunchKernelGGL((k_fp8_gemv_ksplit<R, XR, D, BS, (BS ? 256 : SEG)>), dim3((n + R - 1) / R), \
+                       dim3(256), 0, st, x, w, rs, out, m, n, k)
     if (m <= 2)
-        QP_GEMV_KSPLIT(8, 1);
+        QP_GEMV_KSPLIT(8, 2, SEG_SMALL);
     else if (m <= 4)
-        QP_GEMV_KSPLIT(16, 2);
+        QP_GEMV_KSPLIT(16, 4, SEG_SMALL);
     else if (m <= 8)
-        QP_GEMV_KSPLIT(16, 4);
+        QP_GEMV_KSPLIT(16, 8, SEG_BIG);
     else
-        QP_GEMV_KSPLIT(R16, 8);
+        QP_GEMV_KSPLIT(R16, 16, SEG_BIG);
 #undef QP_GEMV_KSPLIT
 }
 
@@ -541,17 +562,20 @@ static bool gemv_wide(uint32_t n) { return n >= 65536u; }
 
 // Segments in flight per wave for the K-split kernel: two once the grid has
 // several workgroups per CU (measured: N = 17408 gains 4-5% at every M,
-// N = 6144 loses 0-3%), together with 32-row workgroups above M = 8.  The
-// depth changes no summation order.
+// N = 6144 loses 0-3%), together with 32-row workgroups above M = 8 and
+// 128-element segments above M = 4 (half the LDS per workgroup, so more
+// workgroups stay resident: N = 17408, M = 16 26.9 -> 25.9 us; at N = 6144
+// and at M <= 4 they measured equal or slower).  Neither the depth nor the
+// segment size changes any summation order.
 template <bool BS>
 static void launch_gemv_narrow(const uint16_t *x, const uint8_t *w, const float *rs,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                                hipStream_t st)
 {
     if (n >= 12288u)
-        launch_gemv_ksplit<2, BS, 32>(x, w, rs, out, m, n, k, st);
+        launch_gemv_ksplit<2, BS, 32, 256, 128>(x, w, rs, out, m, n, k, st);
     else
-        launch_gemv_ksplit<1, BS, 16>(x, w, rs, out, m, n, k, st);
+        launch_gemv_ksplit<1, BS, 16, 256, 256>(x, w, rs, out, m, n, k, st);
 }
 
 hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
