@@ -359,7 +359,11 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
         }
         // Read back 16-byte units p (physical) of 4 rows per instruction:
         // they hold logical units p ^ ((r % 32) >> 1), with their two
-        // 8-byte halves swapped in odd rows.
+        // 8-byte halves swapped in odd rows.  Other lanes of the wave wrote
+        // them; a wave's LDS operations execute in order, and the
+        // wavefront-scope fence (no instruction) keeps the compiler from
+        // treating the reads as independent of those writes.
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         const int p = lane & 15;
         uint16_t *const obase = out + (size_t)(m0 + wm * 128) * N + n0 + wn * 128;
 #pragma unroll 4
