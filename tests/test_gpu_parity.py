@@ -85,9 +85,13 @@ def test_quantize_bf16_nvfp4_bit_exact(rows, k, scale2):
 # up to 8 chunks per thread, or the two-pass long-row loop; each is run
 # full and ragged (k = 1552, 2064, 6160, 12304 leave part of the last round
 # empty), with row counts that leave the last workgroup's waves partly idle.
+# Thousands of rows (the activation shapes) run with every workgroup resident
+# at once; 4099 and 4133 rows leave the last workgroup partly idle, and
+# k = 1008 and 5136 leave lanes without a chunk.
 @pytest.mark.parametrize("rows,k", [(1, 16), (7, 48), (5, 1024), (6, 1552), (9, 2064),
                                     (4, 4096), (40, 5120), (3, 6144), (2, 6160), (3, 8192),
-                                    (2, 12304), (3, 16384), (3, 20000)])
+                                    (2, 12304), (3, 16384), (3, 20000), (4096, 512),
+                                    (4099, 1008), (4133, 5136), (8192, 5120)])
 def test_quant_rowwise_fp8_bit_exact(rows, k):
     x = _with_edges(_bf16_rows((rows, k), 31 + rows, std=0.02))
     q, s = empty((rows, k), torch.uint8), empty((rows,), torch.float32)
@@ -256,9 +260,12 @@ def test_w4a4_every_scale_code_and_nibble(m, n, k):
 # and the 256 x 256 one (M, N >= 256, K % 128 == 0) with a whole number of
 # its 5-stage unroll (K = 640), a tail of 1 and of 2 stages (K = 128, 896),
 # last tiles shifted back (M = 300, 260; N = 520, 514) and N % 4 != 0 (514:
-# element-wise epilogue everywhere).
+# element-wise epilogue everywhere), and whole multiples of the unroll with
+# shifted last tiles and N % 8 != 0 (K = 1280, 2560: 16-byte stores need
+# N % 8 == 0, so N = 516 stores element-wise).
 @pytest.mark.parametrize("m,n,k", [(130, 200, 272), (256, 384, 1024), (3, 70, 5120), (300, 520, 640),
-                                   (512, 256, 128), (260, 514, 896)])
+                                   (512, 256, 128), (260, 514, 896), (300, 520, 1280),
+                                   (512, 768, 2560), (260, 516, 1280)])
 def test_fp8_gemm_rowscale_matches_oracle(m, n, k):
     a = _bf16_rows((m, k), 61 + m)
     w = _bf16_rows((n, k), 62 + n, std=0.02)
