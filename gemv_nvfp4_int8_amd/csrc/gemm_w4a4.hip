@@ -207,6 +207,8 @@ constexpr int WB_PW = WB_PA + WB_TM * WB_KB;  // 32 KB
 constexpr int WB_SA = WB_PW + WB_TN * WB_KB;  // + 20 KB
 constexpr int WB_SW = WB_SA + WB_TM * WB_NS;  // + 4 KB
 constexpr int WB_BUF = WB_SW + 256 * WB_NS;   // + 4 KB = 60 KB
+constexpr int W4_EPITCH = 2 * WB_TN + 16;     // epilogue staging: bytes per output row
+static_assert(128 * W4_EPITCH <= WB_BUF, "half the output tile fits one stage buffer");
 
 // WM waves along M (2 or 4) times 2 along N: a wave owns RW = 256 / WM rows
 // (NA = RW / 16 MFMA tiles) by 80 columns (5 tiles).  WM = 4 runs two waves
@@ -392,6 +394,39 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     // j = jb + 16*tj + c (c = 0..3).
     const uint32_t ib = m0e + wm * RW + r16;
     const uint32_t jb = n0e + wn * 80 + 4 * g;
+    if (WM == 2 && m0e == m0 && n0e == n0 && N % 8 == 0 &&
+        reinterpret_cast<uintptr_t>(out) % 16 == 0) {
+        // Stored from the MFMA layout, each store would put 32 bytes into
+        // each of 16 rows.  Instead the workgroup stages its 256 x 160 BF16
+        // tile in LDS (rows of 320 bytes at a 336-byte pitch, which spreads
+        // a write's 16 rows over the banks; rows 0-127 in B0, 128-255 in
+        // B1: the last stage ended with every DMA landed and a barrier) and
+        // stores it row-contiguously, 64 consecutive 16-byte chunks (about
+        // three rows) per instruction.
+        uint8_t *const ep = wm == 0 ? B0 : B1;
+#pragma unroll
+        for (int ti = 0; ti < NA; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 5; ++tj) {
+                const f32x4 c = acc[ti][tj];
+                u32x2 pk;
+                pk[0] = pk_bf16(c[0] * s2, c[1] * s2);
+                pk[1] = pk_bf16(c[2] * s2, c[3] * s2);
+                *reinterpret_cast<u32x2 *>(ep + (16 * ti + r16) * W4_EPITCH +
+                                           2 * (wn * 80 + 16 * tj + 4 * g)) = pk;
+            }
+        __syncthreads();
+        uint16_t *const obase = out + (size_t)m0 * N + n0;
+#pragma unroll 4
+        for (int i = 0; i < WB_TN / 8; ++i) {
+            const int idx = threadIdx.x + 256 * i;      // chunk: row idx / 20, 16 bytes idx % 20
+            const int row = idx / (WB_TN / 8), ch = idx % (WB_TN / 8);
+            const uint8_t *src = (row < 128 ? B0 : B1) + (row & 127) * W4_EPITCH + 16 * ch;
+            *reinterpret_cast<u32x4 *>(obase + (size_t)row * N + 8 * ch) =
+                *reinterpret_cast<const u32x4 *>(src);
+        }
+        return;
+    }
     const bool fast = m0e == m0 && n0e == n0 && N % 4 == 0 &&
                       reinterpret_cast<uintptr_t>(out) % 8 == 0;
 #pragma unroll
