@@ -516,15 +516,15 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 // 8-row unit spreads the weight evenly over the CUs; from M = 3 on, the
 // activation rows every workgroup loads outweigh the balance, and 16 rows
 // halve them (measured on N = 6144 and 17408).  Above M = 8 the activation
-// bytes a workgroup reads are twice its weight bytes at 16 rows, and R16
-// rows per workgroup (32 where the grid stays at two or more workgroups per
-// CU) halve them again: N = 17408, M = 16 measured 27.5 -> 26.7 us, while
-// at M = 8 the 32-row grid loses more to its uneven last round than it
-// saves.  (Loading the activations straight into MFMA operand registers
+// bytes a workgroup reads are twice its weight bytes at 16 rows, and 32
+// rows per workgroup halve them again: N = 17408, M = 16 measured 27.5 ->
+// 26.7 us, N = 6144, M = 16 12.1 -> 11.2 us, while at M = 8 the 32-row grid
+// loses more to its uneven last round than it saves (N = 17408: 21.4 ->
+// 23.7 us).  (Loading the activations straight into MFMA operand registers
 // instead of through LDS was slower at every M > 2: each load instruction
 // then touches 16 rows.)  None of these choices changes any row's
 // summation order.
-template <int D, bool BS, int R16, int SEG_SMALL, int SEG_BIG>
+template <int D, bool BS, int SEG_SMALL, int SEG_BIG>
 static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float *rs,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                                hipStream_t st)
@@ -539,7 +539,7 @@ static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float 
     else if (m <= 8)
         QP_GEMV_KSPLIT(16, 8, SEG_BIG);
     else
-        QP_GEMV_KSPLIT(R16, 16, SEG_BIG);
+        QP_GEMV_KSPLIT(32, 16, SEG_BIG);
 #undef QP_GEMV_KSPLIT
 }
 
@@ -562,20 +562,20 @@ static bool gemv_wide(uint32_t n) { return n >= 65536u; }
 
 // Segments in flight per wave for the K-split kernel: two once the grid has
 // several workgroups per CU (measured: N = 17408 gains 4-5% at every M,
-// N = 6144 loses 0-3%), together with 32-row workgroups above M = 8 and
-// 128-element segments above M = 4 (half the LDS per workgroup, so more
-// workgroups stay resident: N = 17408, M = 16 26.9 -> 25.9 us; at N = 6144
-// and at M <= 4 they measured equal or slower).  Neither the depth nor the
-// segment size changes any summation order.
+// N = 6144 loses 0-3%), together with 128-element segments above M = 4
+// (half the LDS per workgroup, so more workgroups stay resident: N = 17408,
+// M = 16 26.9 -> 25.9 us; at N = 6144 and at M <= 4 they measured equal or
+// slower).  Neither the depth nor the segment size changes any summation
+// order.
 template <bool BS>
 static void launch_gemv_narrow(const uint16_t *x, const uint8_t *w, const float *rs,
                                uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
                                hipStream_t st)
 {
     if (n >= 12288u)
-        launch_gemv_ksplit<2, BS, 32, 256, 128>(x, w, rs, out, m, n, k, st);
+        launch_gemv_ksplit<2, BS, 256, 128>(x, w, rs, out, m, n, k, st);
     else
-        launch_gemv_ksplit<1, BS, 16, 256, 256>(x, w, rs, out, m, n, k, st);
+        launch_gemv_ksplit<1, BS, 256, 256>(x, w, rs, out, m, n, k, st);
 }
 
 hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
