@@ -147,7 +147,7 @@ def test_int8_block_partials_bit_exact(m, n, k):
 
 
 def test_w4a8_tiny_pipeline_matches_oracle():
-    """configs: W4A8 tiny (NVFP4 256x512 -> int8/per-32, BF16 acts 16x512)."""
+    """The W4A8 tiny workload (NVFP4 256x512 -> int8/per-32, BF16 acts 16x512)."""
     c = synth.w4a8_tiny("cpu")
     n, k, m = c.n, c.k, c.m
     w_i8, w_s = empty((n, k), torch.int8), empty((n, k // 32), torch.float32)
