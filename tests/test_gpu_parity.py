@@ -279,6 +279,29 @@ def test_fp8_gemm_rowscale_matches_oracle(m, n, k):
     assert_gemm_close(host(out), oracle.fp8_gemm_rowscale(oa, oas, ow, ows), f"fp8 {m}x{n}x{k}")
 
 
+# More 256 x 256 tiles than compute units (289 tiles: a second wave of 33
+# workgroups; 289 % 8 = 1 leaves one tile outside the XCD remap); shifted last
+# tiles with N % 8 != 0 (element-wise epilogue) and with N % 8 == 0 (staged
+# epilogue on the whole tiles, element-wise on the shifted ones).  The
+# oracle computes a sample of rows and columns (each output depends only on
+# its own row pair): random ones plus every row and column of the last two
+# tile rows and columns.
+@pytest.mark.parametrize("m,n,k", [(4352, 4352, 640), (4200, 4100, 640), (4200, 4104, 1280)])
+def test_fp8_gemm_rowscale_many_tiles_matches_oracle(m, n, k):
+    a = _bf16_rows((m, k), 63 + m)
+    w = _bf16_rows((n, k), 64 + n, std=0.02)
+    oa, oas = oracle.quant_rowwise_fp8(bits(a))
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    out = filled((m, n), torch.bfloat16)
+    t = lambda x: dev(torch.from_numpy(x))
+    qp.fp8_gemm_rowscale(t(oa), t(oas), t(ow), t(ows), out)
+    rng = np.random.default_rng(m + n + k)
+    ri = np.union1d(rng.choice(m - 512, 96, replace=False), np.arange(m - 512, m))
+    ci = np.union1d(rng.choice(n - 512, 96, replace=False), np.arange(n - 512, n))
+    ref = oracle.fp8_gemm_rowscale(oa[ri], oas[ri], ow[ci], ows[ci])
+    assert_gemm_close(host(out)[np.ix_(ri, ci)], ref, f"fp8 {m}x{n}x{k}")
+
+
 def test_fp8_rowwise_proj_block_and_passthrough():
     m, n, k = 70, 256, 512
     cse = synth.fp8_block("cpu", m=m, n=n, k=k)
