@@ -13,6 +13,24 @@
 namespace qp {
 static std::atomic<uint64_t> g_launches{0};
 void count_launch(uint32_t n) { g_launches.fetch_add(n, std::memory_order_relaxed); }
+
+uint32_t cu_count()
+{
+    constexpr int MAXDEV = 64;
+    static std::atomic<uint32_t> cached[MAXDEV] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV)
+        return 0;
+    uint32_t c = cached[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            return 0;
+        c = (uint32_t)v;
+        cached[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
 } // namespace qp
 
 namespace {

@@ -291,20 +291,23 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 // branch, so the compiler counts the loads in flight exactly and waits only
 // for the stage it is about to use.
 // ---------------------------------------------------------------------------
-template <int R, int NW, int NX>
+template <int RC, int NW, int NX>
 struct GvSegK {
     u32x4 w[NW];         // R weight rows of the segment, 1 KB per instruction
     u32x4 x[NX];         // XR activation rows of the segment, 1 KB per instruction
     float s[2];          // block scales of the segment's two K blocks (BS)
 };
 
-template <int R, int XR, int D, bool BS, int SEG>
+template <int RC, int XR, int D, bool BS, int SEG>
 __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w,
     const float *__restrict__ rs, uint16_t *__restrict__ out,
-    uint32_t m, uint32_t n, uint32_t k)
+    uint32_t m, uint32_t n, uint32_t k, uint32_t rpw)
 {
-    static_assert(R == 8 || R == 16 || R == 32, "8, 16 or 32 rows per workgroup");
+    // RC rows of capacity per workgroup, of which the first rpw are live
+    // (rpw = RC with block scales, whose scale row must be the workgroup's)
+    constexpr int R = RC;
+    static_assert(RC == 8 || (RC % 16 == 0 && RC <= 80), "8 or a multiple of 16 up to 80 rows");
     static_assert(XR == 2 || XR == 4 || XR == 8 || XR == 16, "2, 4, 8 or 16 activation rows");
     static_assert(SEG == 256 || (SEG == 128 && !BS), "256-element segments, or 128 without block scales");
     // MFMA weight tiles of 16 rows (R = 8: one, its rows 8..15 zero)
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const uint32_t row0 = blockIdx.x * R;
+    const uint32_t row0 = blockIdx.x * rpw;
     // K quarters end on 256-element boundaries whatever SEG is, so that a
     // row's summation order never depends on the launch shape.
     const uint32_t per = ((k + 255) / 256 + 3) / 4 * (256 / SEG);
@@ -344,8 +347,8 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     uint32_t wofs[NW];
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-        const uint32_t r = row0 + WRPI * j + wr0;
-        wofs[j] = r < n ? r * k + 16 * wc : OOB;
+        const uint32_t rl = WRPI * j + wr0, r = row0 + rl;
+        wofs[j] = rl < rpw && r < n ? r * k + 16 * wc : OOB;
     }
     // activation instruction i: row XRPI i + lane / XCH, elements
     // 8 (lane % XCH) .. +7 of the segment
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         xofs[i] = r < m ? 2 * (r * k + 8 * xc) : OOB;
     }
 
-    auto load = [&](GvSegK<R, NW, NX> &g, uint32_t seg) {
+    auto load = [&](GvSegK<RC, NW, NX> &g, uint32_t seg) {
         const bool live = seg < s_end;
         const uint32_t kb = seg * SEG;
         if constexpr (BS) {
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
             g.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                 xr, xlive ? xofs[i] + 2 * kb : OOB, 0, 0));
     };
-    auto stash = [&](const GvSegK<R, NW, NX> &g) {
+    auto stash = [&](const GvSegK<RC, NW, NX> &g) {
 #pragma unroll
         for (int j = 0; j < NW; ++j)
             *reinterpret_cast<u32x4 *>(&sw[wave][(WRPI * j + wr0) * WPITCH + 16 * wc]) = g.w[j];
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     // D stages in flight.  The loop is unrolled by D so every stage is a
     // statically named variable: stage d holds segment seg + d, and is
     // reloaded with segment seg + d + D as soon as it has been stashed.
-    GvSegK<R, NW, NX> g[D];
+    GvSegK<RC, NW, NX> g[D];
 #pragma unroll
     for (int d = 0; d < D; ++d)
         load(g[d], s_beg + d);
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         for (int v = 0; v < 3; ++v)
             acc[t] += red[v][t][lane];
         const uint32_t nn = row0 + 16 * t + col;
-        if (col < R && nn < n) {
+        if (16 * t + col < (int)rpw && nn < n) {
             const float sc = BS ? 1.0f : rs[nn];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -512,35 +515,102 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     }
 }
 
-// Rows per workgroup and activation row pairs follow M: at M <= 2 the
-// 8-row unit spreads the weight evenly over the CUs; from M = 3 on, the
-// activation rows every workgroup loads outweigh the balance, and 16 rows
-// halve them (measured on N = 6144 and 17408).  Above M = 8 the activation
-// bytes a workgroup reads are twice its weight bytes at 16 rows, and 32
-// rows per workgroup halve them again: N = 17408, M = 16 measured 27.5 ->
-// 26.7 us, N = 6144, M = 16 12.1 -> 11.2 us, while at M = 8 the 32-row grid
-// loses more to its uneven last round than it saves (N = 17408: 21.4 ->
-// 23.7 us).  (Loading the activations straight into MFMA operand registers
-// instead of through LDS was slower at every M > 2: each load instruction
-// then touches 16 rows.)  None of these choices changes any row's
-// summation order.
-template <int D, bool BS, int SEG_SMALL, int SEG_BIG>
-static void launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float *rs,
-                               uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
-                               hipStream_t st)
+// Rows per workgroup.  Every workgroup reads the activation rows of its K
+// range once, so more rows per workgroup means fewer activation bytes per
+// weight byte; but a narrow grid is short (a few microseconds), and when
+// some CUs get one workgroup more than others those CUs set the time (N =
+// 17408 in 32-row workgroups is 544 of them on 256 CUs: 26.0 us, against
+// 20.1 us for N = 16384's 512).  So above M = 2 the grid is a whole number
+// j of workgroups per CU, each with rpw = ceil(N / (j CUs)) live rows in a
+// capacity of 8 or a multiple of 16 rows (up to 80), and j follows M:
+//   - M <= 2: 8 rows (the weight dominates; the 8-row unit already spreads
+//     evenly, and the activation pair is small);
+//   - M <= 4: about 16 rows per workgroup (N = 6144: 12 rows on 512
+//     workgroups, 8.4 -> 7.9 us);
+//   - M <= 8: two workgroups per CU (N = 17408: 34 rows, 21.5 -> 19.6 us;
+//     N = 6144: 12 rows, 9.6 -> 9.1 us);
+//   - M <= 16: one workgroup per CU while its rows fit (N = 17408: 68 rows,
+//     26.0 -> 22.0 us; N = 12288: 48 rows, 18.9 -> 16.4 us).
+// Block scales need a workgroup's rows inside one 128-row scale block, so
+// that path keeps 8, 16 or 32 rows.  (Loading the activations straight
+// into MFMA operand registers instead of through LDS was slower at every
+// M > 2: each load instruction then touches 16 rows.)  None of these
+// choices changes any row's summation order.
+struct GvSplit {
+    uint32_t rc, rpw;
+};
+static GvSplit gemv_split(uint32_t n, uint32_t m, bool bs)
 {
-#define QP_GEMV_KSPLIT(R, XR, SEG)                                                          \
-    hipLaunchKernelGGL((k_fp8_gemv_ksplit<R, XR, D, BS, (BS ? 256 : SEG)>), dim3((n + R - 1) / R), \
-                       dim3(256), 0, st, x, w, rs, out, m, n, k)
+    const uint32_t cus = cu_count();
+    if (bs || m <= 2 || cus == 0) {
+        const uint32_t r = m <= 2 ? 8 : m <= 8 ? 16 : 32;
+        return GvSplit{r, r};
+    }
+    const uint32_t div = cus * (m <= 4 ? 16 : 80);
+    uint32_t j = (n + div - 1) / div;
+    if (m > 4 && m <= 8 && j < 2)
+        j = 2;
+    uint32_t rpw = (n + cus * j - 1) / (cus * j);
+    const uint32_t lo = m <= 4 ? 8 : 12;
+    rpw = rpw < lo ? lo : rpw;
+    return GvSplit{rpw <= 8 ? 8 : (rpw + 15) / 16 * 16, rpw};
+}
+
+// The (capacity, activation rows) pairs gemv_split can ask for; any other
+// pair is an internal error, never a silent no-op.
+template <int RC, int XR, bool BS>
+constexpr bool ksplit_shape_ok()
+{
+    if (BS)
+        return RC == (XR <= 2 ? 8 : XR <= 8 ? 16 : 32);
+    return XR == 2 ? RC == 8 : XR == 4 ? RC <= 16 : RC >= 16;
+}
+
+template <int RC, int XR, int D, bool BS, int SEG>
+static hipError_t launch_ksplit_rc(const uint16_t *x, const uint8_t *w, const float *rs,
+                                   uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                   uint32_t rpw, hipStream_t st)
+{
+    if constexpr (ksplit_shape_ok<RC, XR, BS>()) {
+        hipLaunchKernelGGL((k_fp8_gemv_ksplit<RC, XR, D, BS, (BS ? 256 : SEG)>),
+                           dim3((n + rpw - 1) / rpw), dim3(256), 0, st, x, w, rs, out, m, n, k, rpw);
+        return hipSuccess;
+    } else {
+        return hipErrorInvalidConfiguration;
+    }
+}
+
+template <int XR, int D, bool BS, int SEG>
+static hipError_t launch_ksplit_xr(const uint16_t *x, const uint8_t *w, const float *rs,
+                                   uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                   GvSplit sp, hipStream_t st)
+{
+    if (sp.rpw == 0 || sp.rpw > sp.rc)
+        return hipErrorInvalidConfiguration;
+    switch (sp.rc) {
+    case 8: return launch_ksplit_rc<8, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+    case 16: return launch_ksplit_rc<16, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+    case 32: return launch_ksplit_rc<32, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+    case 48: return launch_ksplit_rc<48, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+    case 64: return launch_ksplit_rc<64, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+    case 80: return launch_ksplit_rc<80, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+    default: return hipErrorInvalidConfiguration;
+    }
+}
+
+template <int D, bool BS, int SEG_SMALL, int SEG_BIG>
+static hipError_t launch_gemv_ksplit(const uint16_t *x, const uint8_t *w, const float *rs,
+                                     uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                     hipStream_t st)
+{
+    const GvSplit sp = gemv_split(n, m, BS);
     if (m <= 2)
-        QP_GEMV_KSPLIT(8, 2, SEG_SMALL);
-    else if (m <= 4)
-        QP_GEMV_KSPLIT(16, 4, SEG_SMALL);
-    else if (m <= 8)
-        QP_GEMV_KSPLIT(16, 8, SEG_BIG);
-    else
-        QP_GEMV_KSPLIT(32, 16, SEG_BIG);
-#undef QP_GEMV_KSPLIT
+        return launch_ksplit_xr<2, D, BS, SEG_SMALL>(x, w, rs, out, m, n, k, sp, st);
+    if (m <= 4)
+        return launch_ksplit_xr<4, D, BS, SEG_SMALL>(x, w, rs, out, m, n, k, sp, st);
+    if (m <= 8)
+        return launch_ksplit_xr<8, D, BS, SEG_BIG>(x, w, rs, out, m, n, k, sp, st);
+    return launch_ksplit_xr<16, D, BS, SEG_BIG>(x, w, rs, out, m, n, k, sp, st);
 }
 
 template <int T, int D, bool BS>
@@ -568,24 +638,26 @@ static bool gemv_wide(uint32_t n) { return n >= 65536u; }
 // slower).  Neither the depth nor the segment size changes any summation
 // order.
 template <bool BS>
-static void launch_gemv_narrow(const uint16_t *x, const uint8_t *w, const float *rs,
-                               uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
-                               hipStream_t st)
+static hipError_t launch_gemv_narrow(const uint16_t *x, const uint8_t *w, const float *rs,
+                                     uint16_t *out, uint32_t m, uint32_t n, uint32_t k,
+                                     hipStream_t st)
 {
     if (n >= 12288u)
-        launch_gemv_ksplit<2, BS, 256, 128>(x, w, rs, out, m, n, k, st);
-    else
-        launch_gemv_ksplit<1, BS, 256, 256>(x, w, rs, out, m, n, k, st);
+        return launch_gemv_ksplit<2, BS, 256, 128>(x, w, rs, out, m, n, k, st);
+    return launch_gemv_ksplit<1, BS, 256, 256>(x, w, rs, out, m, n, k, st);
 }
 
 hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
                                     const float *rs, uint16_t *out, uint32_t m,
                                     uint32_t n, uint32_t k, hipStream_t st)
 {
-    if (gemv_wide(n))
+    if (gemv_wide(n)) {
         launch_gemv_rows<2, 1, false>(x, w, rs, out, m, n, k, st);
-    else
-        launch_gemv_narrow<false>(x, w, rs, out, m, n, k, st);
+    } else {
+        const hipError_t e = launch_gemv_narrow<false>(x, w, rs, out, m, n, k, st);
+        if (e != hipSuccess)
+            return e;
+    }
     count_launch();
     return hipGetLastError();
 }
@@ -595,10 +667,13 @@ hipError_t launch_fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
                                       const float *grid, uint16_t *out, uint32_t m,
                                       uint32_t n, uint32_t k, hipStream_t st)
 {
-    if (gemv_wide(n))
+    if (gemv_wide(n)) {
         launch_gemv_rows<2, 1, true>(x, w, grid, out, m, n, k, st);
-    else
-        launch_gemv_narrow<true>(x, w, grid, out, m, n, k, st);
+    } else {
+        const hipError_t e = launch_gemv_narrow<true>(x, w, grid, out, m, n, k, st);
+        if (e != hipSuccess)
+            return e;
+    }
     count_launch();
     return hipGetLastError();
 }

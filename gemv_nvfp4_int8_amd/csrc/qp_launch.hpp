@@ -51,4 +51,8 @@ hipError_t launch_w4a4_gemm(const uint8_t *ap, const uint8_t *asc,
 // Counts kernel launches enqueued by the library (all launchers add to it).
 void count_launch(uint32_t n = 1);
 
+// Compute units of the current device, queried once per device; 0 if the
+// query fails (launch shapes that depend on it then take a fixed default).
+uint32_t cu_count();
+
 } // namespace qp

@@ -375,6 +375,34 @@ def test_fp8_gemv_wide_and_partial_segments(n, k):
         assert_gemv_close(host(out), oracle.fp8_gemv_rowscale(bits(x[:m]), ow, ows), f"gemv {n}x{k} m={m}")
 
 
+# Narrow weights above M = 2 take a whole number of workgroups per CU, each
+# with ceil(N / workgroups) live rows inside a capacity of 16 to 80 rows.  On
+# a 256-CU part these N reach every capacity: 12288 (48 rows at M > 8),
+# 16384 (64), 17408 (68 live of 80 at M > 8, 34 of 48 at M <= 8, 14 of 16
+# at M <= 4), 20481 (41 of 48, ragged last workgroup), 40000 (79 of 80).  The
+# whole output is checked against the oracle, and every row of an M-row call
+# equals the M = 1 call on that row bit for bit.
+@pytest.mark.parametrize("n", [12288, 16384, 17408, 20481, 40000])
+def test_fp8_gemv_balanced_row_split(n):
+    k = 1040
+    w = synth.gemv_weight_bf16(n, k, "cpu", shape_id=3)
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    wq, ws = dev(torch.from_numpy(ow)), dev(torch.from_numpy(ows))
+    x = synth.gemv_acts_bf16(16, k, "cpu", shape_id=3)
+    xd = dev(x)
+    singles = []
+    for i in range(16):
+        o = empty((1, n), torch.bfloat16)
+        qp.fp8_gemv_rowscale(xd[i:i + 1], wq, ws, o)
+        singles.append(o)
+    single = torch.cat(singles)
+    for m in (3, 5, 8, 9, 16):
+        out = filled((m, n), torch.bfloat16)
+        qp.fp8_gemv_rowscale(xd[:m], wq, ws, out)
+        assert_gemv_close(host(out), oracle.fp8_gemv_rowscale(bits(x[:m]), ow, ows), f"gemv {n} m={m}")
+        assert torch.equal(out.view(torch.int16), single[:m].view(torch.int16)), m
+
+
 # ---------------------------------------------------------------------------
 # Block-scaled FP8 GEMV (fp8_gemv_batch.rs, w8a16_gemv_batch4 / _batch2).
 @pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (384, 1152), (6144, 5120),
