@@ -102,8 +102,8 @@ struct W4Src {
     uint32_t kc;            // K index of the lane's chunk within a window
 
     __device__ __forceinline__ void init(const uint16_t *x, const uint8_t *wp, const uint8_t *ws,
-                                         uint32_t row0, uint32_t m, uint32_t n, uint32_t k,
-                                         int lane)
+                                         uint32_t row0, uint32_t rpv, uint32_t m, uint32_t n,
+                                         uint32_t k, int lane)
     {
         rw = make_rsrc(wp, n * (k / 2));
         rs = make_rsrc(ws, n * (k / 16));
@@ -111,8 +111,8 @@ struct W4Src {
         kc = 32 * (lane / 4);
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-            uint32_t r = row0 + 4 * rg + lane % 4;
-            wo[rg] = r < n ? r * (k / 2) + kc / 2 : W4_OOB;
+            uint32_t q = 4 * rg + lane % 4, r = row0 + q;
+            wo[rg] = q < rpv && r < n ? r * (k / 2) + kc / 2 : W4_OOB;
         }
     }
     // The packed codes of window `win`; lanes whose 32-element chunk lies
@@ -190,17 +190,19 @@ __device__ __forceinline__ void w4_block_sum(f32x4 (*acc)[MG])
             }
 }
 
-// Lanes 0..3: C[4g + i][row0 + 4rg + lane] = bf16(acc * scale2).
+// Lanes 0..3: C[4g + i][row0 + 4rg + lane] = bf16(acc * scale2), for the
+// wave's rpv live rows.
 template <int MG, int RG>
 __device__ __forceinline__ void w4_store(f32x4 (*acc)[MG], float scale2, uint16_t *out,
-                                         uint32_t row0, uint32_t m, uint32_t n, int lane)
+                                         uint32_t row0, uint32_t rpv, uint32_t m, uint32_t n,
+                                         int lane)
 {
     if (lane >= 4)
         return;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         uint32_t nn = row0 + 4 * rg + lane;
-        if (nn >= n)
+        if (4 * rg + lane >= (int)rpv || nn >= n)
             continue;
 #pragma unroll
         for (int g = 0; g < MG; ++g)
@@ -243,8 +245,9 @@ template <int MG, int RG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5 : 1))) void k_w4a16_gemv_rows(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
     const uint8_t *__restrict__ ws, float scale2, uint16_t *__restrict__ out,
-    uint32_t m, uint32_t n, uint32_t k)
+    uint32_t m, uint32_t n, uint32_t k, uint32_t rpv)
 {
+    // each wave holds ROWS rows, of which the first rpv are live
     constexpr int ROWS = 4 * RG;
     constexpr int WG_ROWS = 4 * ROWS;
     constexpr int XC = MG;                  // activation chunks per thread and window
@@ -254,13 +257,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const uint32_t wg_row0 = blockIdx.x * WG_ROWS;
-    const uint32_t row0 = wg_row0 + wave * ROWS;
+    const uint32_t wg_row0 = blockIdx.x * 4 * rpv;
+    const uint32_t row0 = wg_row0 + wave * rpv;
     const uint32_t nwin = (k + W4_WIN - 1) / W4_WIN;
     const uint32_t srow = k / 16;           // scale bytes per row
 
     W4Src<MG, RG> src;
-    src.init(x, wp, ws, row0, m, n, k, lane);
+    src.init(x, wp, ws, row0, rpv, m, n, k, lane);
     // staged activation chunk c = tid + 256 j: row c / 64, elements 8 (c % 64) ..
     buf_rsrc rx = src.rx;
     uint32_t xso[XC], xke[XC];
@@ -279,18 +282,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
             v[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xso[j] + dx, 0, 0);
         }
     };
-    // staged scale chunk c = tid + 256 j: workgroup row c / 8, bytes 8 (c % 8)
-    // of the row's 64-byte group segment; chunks beyond the rows (or, for
-    // a workgroup of one row group, beyond the 128 RG chunks) read zero.
+    // staged scale chunk c = tid + 256 j: LDS row c / 8 (row q = c/8 % ROWS
+    // of wave c/8 / ROWS, live if q < rpv), bytes 8 (c % 8) of the row's
+    // 64-byte group segment; chunks beyond the rows (or, for a workgroup of
+    // one row group, beyond the 128 RG chunks) read zero.
     buf_rsrc rs = src.rs;
-    uint32_t sso[SCH], sbo[SCH];
+    uint32_t sso[SCH], sbo[SCH], gr_of[SCH];
     int slo[SCH];
 #pragma unroll
     for (int j = 0; j < SCH; ++j) {
         int c = tid + 256 * j, r = c >> 3;
         sbo[j] = 8 * (c & 7);
-        uint32_t gr = wg_row0 + r;
-        sso[j] = (c < WG_ROWS * 8 && gr < n) ? gr * srow + sbo[j] : W4_OOB;
+        const uint32_t q = r % ROWS;
+        gr_of[j] = wg_row0 + (r / ROWS) * rpv + q;
+        sso[j] = (c < WG_ROWS * 8 && q < rpv && gr_of[j] < n) ? gr_of[j] * srow + sbo[j] : W4_OOB;
         slo[j] = r * W4_GB + sbo[j];
     }
     // Scale bytes at or beyond k/16 in a row are zeroed in registers (an
@@ -309,8 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
     const uint32_t fix_d = ((srow - 2) % 8) / 4;
 #pragma unroll
     for (int j = 0; j < SCH; ++j) {
-        const bool owner = srow % 4 == 2 && sso[j] < W4_OOB &&
-                           wg_row0 + ((tid + 256 * j) >> 3) == n - 1 &&
+        const bool owner = srow % 4 == 2 && sso[j] < W4_OOB && gr_of[j] == n - 1 &&
                            (srow - 2) % W4_GB / 8 * 8 == sbo[j];
         fix_g[j] = owner ? (srow - 2) / W4_GB : ~0u;
     }
@@ -398,25 +402,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
         step(A, xa, win, 0, sb, 0);
     }
     w4_block_sum<MG, RG>(acc);
-    w4_store<MG, RG>(acc, scale2, out, row0, m, n, lane);
+    w4_store<MG, RG>(acc, scale2, out, row0, rpv, m, n, lane);
 }
 
 // Row groups per wave, from n alone (never m): two (8 weight rows) for wide
-// weights; one (4 rows) for narrow ones, so that they still spread over all
-// CUs (N = 6144: 384 workgroups of 16 rows).  Measured at K = 5120 against the
-// earlier K-split kernel for narrow weights (four waves sharing 8 rows, each
-// a quarter of K): N = 17408, M = 1 / 2 / 8: 17.4 / 18.6 / 36.5 -> 12.5 /
-// 12.9 / 18.8 us; N = 6144: 8.3 / 8.9 / 15.2 -> 7.4 / 7.5 / 9.2 us.
+// weights; one (4 rows, or 3 live rows of 4, below) for narrow ones, so that
+// they still spread over all CUs (N = 6144: 384 workgroups of 16 rows).
+// Measured at K = 5120 against an earlier K-split kernel for narrow weights
+// (four waves sharing 8 rows, each a quarter of K): N = 17408, M = 1 / 2 /
+// 8: 17.4 / 18.6 / 36.5 -> 12.5 / 12.9 / 18.8 us; N = 6144: 8.3 / 8.9 / 15.2
+// -> 7.4 / 7.5 / 9.2 us.  A second K-split form (rows per workgroup sized to
+// the CUs, wave-private activation windows, no barrier, three windows in
+// flight) was also slower at every measured shape (N = 17408, M = 1: 16.7
+// us; N = 6144, M = 1: 7.9 us), its registers capping residency.
 static bool w4_gemv_wide(uint32_t n) { return n >= 65536u; }
 
 template <int MG, int RG>
 static void launch_w4(const uint16_t *x, const uint8_t *wp, const uint8_t *ws, float scale2,
-                      uint16_t *out, uint32_t m, uint32_t n, uint32_t k, hipStream_t st)
+                      uint16_t *out, uint32_t m, uint32_t n, uint32_t k, uint32_t rpv,
+                      hipStream_t st)
 {
-    constexpr uint32_t ROWS = 4 * RG;
-    const uint32_t grid = (n + 4 * ROWS - 1) / (4 * ROWS);
+    const uint32_t grid = (n + 4 * rpv - 1) / (4 * rpv);
     hipLaunchKernelGGL((k_w4a16_gemv_rows<MG, RG>), dim3(grid), dim3(256), 0, st,
-                       x, wp, ws, scale2, out, m, n, k);
+                       x, wp, ws, scale2, out, m, n, k, rpv);
+}
+
+// Live rows per wave for narrow weights: 4, or 3 when that cuts the rows on
+// the busiest CU by at least a quarter (a narrow grid is short, and the CUs
+// holding one workgroup more than the others set its time; a wave with 3
+// live rows of 4 issues a third more per row, which the cut must repay).
+// N = 6144: 384 workgroups of 16 rows put 32 rows on some CUs, 512 of 12
+// rows put 24 on every CU (M = 8: 9.2 -> 9.0 us, M = 1, 2 equal).  N =
+// 17408 (80 -> 72 rows) measured slower with 3 (M = 1: 12.5 -> 13.3 us).
+static uint32_t w4_rows_per_wave(uint32_t n)
+{
+    const uint32_t cus = cu_count();
+    if (cus == 0)
+        return 4;
+    auto busiest = [&](uint32_t rpv) {
+        const uint32_t wgs = (n + 4 * rpv - 1) / (4 * rpv);
+        return (wgs + cus - 1) / cus * 4 * rpv;
+    };
+    return 4 * busiest(3) <= 3 * busiest(4) ? 3 : 4;
 }
 
 // 1 <= m <= 8, k % 32 == 0 and every buffer < 2^30 bytes (checked by the
@@ -426,12 +453,13 @@ hipError_t launch_w4a16_gemv(const uint16_t *x, const uint8_t *wp, const uint8_t
                              uint32_t k, hipStream_t st)
 {
     const bool wide = w4_gemv_wide(n);
+    const uint32_t rpv = wide ? 8 : w4_rows_per_wave(n);
     if (m <= 4)
-        wide ? launch_w4<1, 2>(x, wp, ws, scale2, out, m, n, k, st)
-             : launch_w4<1, 1>(x, wp, ws, scale2, out, m, n, k, st);
+        wide ? launch_w4<1, 2>(x, wp, ws, scale2, out, m, n, k, rpv, st)
+             : launch_w4<1, 1>(x, wp, ws, scale2, out, m, n, k, rpv, st);
     else
-        wide ? launch_w4<2, 2>(x, wp, ws, scale2, out, m, n, k, st)
-             : launch_w4<2, 1>(x, wp, ws, scale2, out, m, n, k, st);
+        wide ? launch_w4<2, 2>(x, wp, ws, scale2, out, m, n, k, rpv, st)
+             : launch_w4<2, 1>(x, wp, ws, scale2, out, m, n, k, rpv, st);
     count_launch();
     return hipGetLastError();
 }
