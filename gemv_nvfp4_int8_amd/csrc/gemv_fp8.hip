@@ -271,18 +271,21 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 
 // ---------------------------------------------------------------------------
 // Narrow weights: too few rows to give every CU several workgroups, so the
-// four waves of a workgroup share R rows (8, 16 or 32) and split K into
-// contiguous quarters (ending on 256-element boundaries).  Everything is
-// wave-private (the weight transpose tile and the activation segment live in
-// the wave's own LDS region, so the loop has no barrier), D segments of SEG
-// K elements are loaded ahead, and the four partial tiles are added in a
-// fixed order at the end.
+// four waves of a workgroup share its rows and split K into contiguous
+// quarters (ending on 256-element boundaries).  Everything is wave-private
+// (the weight transpose tile and the activation segment live in the wave's
+// own LDS region, so the loop has no barrier), D segments of SEG K elements
+// are loaded ahead, and the four partial tiles are added in a fixed order at
+// the end.
 //
-// R = 8 halves the work unit so that narrow weights spread evenly over the
-// CUs (N = 6144: 768 workgroups, three per CU, against 384 of 16 rows); the
-// MFMA's weight rows 8..15 then read an all-zero LDS row.  XR activation
-// rows are loaded per segment (M <= XR); the rows past them likewise read a
-// zero row.  None of R, XR, D and SEG changes any summation order.
+// A workgroup has a capacity of RC rows (8, or a multiple of 16 up to 80:
+// RC / 16 MFMA row tiles) of which the first rpw are live; rows past them
+// read zero.  The launcher sizes rpw so that the grid is a whole number of
+// workgroups per CU.  RC = 8 halves the work unit (N = 6144: 768
+// workgroups, three per CU); the MFMA's weight rows 8..15 then read an
+// all-zero LDS row.  XR activation rows are loaded per segment (M <= XR);
+// the rows past them likewise read a zero row.  None of RC, rpw, XR, D and
+// SEG changes any summation order.
 //
 // Every load is a raw buffer load from a 32-bit offset (n*k < 2^31,
 // m*k < 2^31).  Rows past N, bytes past K, activation rows past M and
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 // ---------------------------------------------------------------------------
 template <int RC, int NW, int NX>
 struct GvSegK {
-    u32x4 w[NW];         // R weight rows of the segment, 1 KB per instruction
+    u32x4 w[NW];         // RC weight rows of the segment, 1 KB per instruction
     u32x4 x[NX];         // XR activation rows of the segment, 1 KB per instruction
     float s[2];          // block scales of the segment's two K blocks (BS)
 };
