@@ -38,11 +38,12 @@
 //    wave.  The four waves of a workgroup stage the window in LDS once
 //    (double-buffered, one barrier per window) instead of each fetching it
 //    from L2.
-//  * Two register stages are used in turn, so each wave keeps the next two
-//    windows in flight.  Every load is a raw buffer load: a lane whose data
-//    does not exist (rows >= n or >= m, K past the end, a prefetch past the
-//    last window) gets an offset beyond the buffer and reads zero without
-//    touching memory, so no load sits under a branch.
+//  * Two register stages (four for small narrow grids) are used in turn, so
+//    each wave keeps the next two (four) windows in flight.  Every load is a
+//    raw buffer load: a lane whose data does not exist (rows >= n or >= m, K
+//    past the end, a prefetch past the last window) gets an offset beyond
+//    the buffer and reads zero without touching memory, so no load sits
+//    under a branch.
 //  * Each wave owns 4 or 8 rows (chosen from N alone) over all of K.  No
 //    summation order depends on M, so every output row is bit-identical to
 //    an M = 1 call on that row.
@@ -241,13 +242,14 @@ constexpr int W4_GB = W4_GW * W4_SB;        // scale bytes per row per group (64
 // waves per SIMD (<= 102 VGPRs); the two-group kernel is left to the
 // compiler, whose unconstrained schedule keeps the scale and activation
 // loads in flight across the window barrier (measured).
-template <int MG, int RG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5 : 1))) void k_w4a16_gemv_rows(
+template <int MG, int RG, int ST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 && ST == 2 ? 5 : 1))) void k_w4a16_gemv_rows(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ wp,
     const uint8_t *__restrict__ ws, float scale2, uint16_t *__restrict__ out,
     uint32_t m, uint32_t n, uint32_t k, uint32_t rpv)
 {
     // each wave holds ROWS rows, of which the first rpv are live
+    static_assert(ST == 2 || ST == 4, "two or four register stages");
     constexpr int ROWS = 4 * RG;
     constexpr int WG_ROWS = 4 * ROWS;
     constexpr int XC = MG;                  // activation chunks per thread and window
@@ -365,42 +367,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
     f32x4 acc[RG][MG];
     w4_zero<MG, RG>(acc);
 
-    W4Wts<RG> A, B;
-    u32x4 xa[XC], xb[XC];
+    // ST register stages, each holding one window's weights and staged
+    // activations; window w lives in stage w % ST and its stage is refilled
+    // with window w + ST as soon as it has been used.
+    W4Wts<RG> S[ST];
+    u32x4 X[ST][XC];
     u32x2 sg[SCH];
     load_sg(sg, 0);
-    src.load_w(A, 0, nwin > 0, k);
-    load_xs(xa, 0, nwin > 0);
-    src.load_w(B, 1, nwin > 1, k);
-    load_xs(xb, 1, nwin > 1);
+#pragma unroll
+    for (int d = 0; d < ST; ++d) {
+        src.load_w(S[d], d, (uint32_t)d < nwin, k);
+        load_xs(X[d], d, (uint32_t)d < nwin);
+    }
     W4Act<MG> frag;
 
-    // One window: stage its activations, prefetch the window two ahead,
+    // One window: stage its activations, prefetch the window ST ahead,
     // synchronise, compute.
     auto step = [&](W4Wts<RG> &W, u32x4 *xs, uint32_t w, int buf, int sb, int wig) {
 #pragma unroll
         for (int j = 0; j < XC; ++j)
             *reinterpret_cast<u32x4 *>(&sx[buf][xlo[j]]) = xs[j];
-        load_xs(xs, w + 2, w + 2 < nwin);
+        load_xs(xs, w + ST, w + ST < nwin);
         __syncthreads();
         read_frags(frag, buf);
         read_scales(W, sb, wig);
         w4_window<MG, RG>(acc, W, frag);
-        src.load_w(W, w + 2, w + 2 < nwin, k);
+        src.load_w(W, w + ST, w + ST < nwin, k);
+    };
+    // Scale groups are window pairs: group g (windows 2g, 2g + 1) is staged
+    // in ss[g % 2] before its first window, and the next group is fetched.
+    // ST is even, so a window's activation buffer and its half of the
+    // group follow from its stage.
+    auto window = [&](int d, uint32_t w) {
+        const uint32_t grp = w / 2;
+        const int sb = grp & 1;
+        if (d % 2 == 0) {
+            stash_sg(sg, grp, sb);
+            load_sg(sg, grp + 1);
+        }
+        step(S[d], X[d], w, d & 1, sb, d & 1);
     };
     uint32_t win = 0;
-    for (; win + 2 <= nwin; win += 2) {
-        const int sb = (win / 2) & 1;
-        stash_sg(sg, win / 2, sb);
-        load_sg(sg, win / 2 + 1);
-        step(A, xa, win, 0, sb, 0);
-        step(B, xb, win + 1, 1, sb, 1);
-    }
-    if (win < nwin) {               // an odd last window, already in A
-        const int sb = (win / 2) & 1;
-        stash_sg(sg, win / 2, sb);
-        step(A, xa, win, 0, sb, 0);
-    }
+    for (; win + ST <= nwin; win += ST)
+#pragma unroll
+        for (int d = 0; d < ST; ++d)
+            window(d, win + d);
+#pragma unroll
+    for (int d = 0; d < ST; ++d)    // the last windows, fewer than ST
+        if (win + d < nwin)
+            window(d, win + d);
     w4_block_sum<MG, RG>(acc);
     w4_store<MG, RG>(acc, scale2, out, row0, rpv, m, n, lane);
 }
@@ -417,14 +432,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MG == 1 ? 5
 // us; N = 6144, M = 1: 7.9 us), its registers capping residency.
 static bool w4_gemv_wide(uint32_t n) { return n >= 65536u; }
 
+// Register stages: four (window loads four ahead) for the one-group kernel
+// when the whole grid is resident at its 146 registers, i.e. at most three
+// workgroups per CU; two otherwise.  Narrow grids are a few memory round
+// trips long, and the deeper prefetch removes some of them: N = 6144, M = 1 /
+// 2: 7.7 / 7.8 -> 7.0 / 7.1 us; N = 12288: 9.2 -> 9.0 us.  Where the grid
+// needs more rounds (N = 17408: 12.5 -> 14.3 us) or at two activation groups
+// (218 registers; N = 6144, M = 8: 8.5 -> 9.5 us) four stages lose.  The
+// stage count changes no summation order.
+template <int MG, int RG, int ST>
+static void launch_w4_st(const uint16_t *x, const uint8_t *wp, const uint8_t *ws, float scale2,
+                         uint16_t *out, uint32_t m, uint32_t n, uint32_t k, uint32_t rpv,
+                         uint32_t grid, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_w4a16_gemv_rows<MG, RG, ST>), dim3(grid), dim3(256), 0, st,
+                       x, wp, ws, scale2, out, m, n, k, rpv);
+}
+
 template <int MG, int RG>
 static void launch_w4(const uint16_t *x, const uint8_t *wp, const uint8_t *ws, float scale2,
                       uint16_t *out, uint32_t m, uint32_t n, uint32_t k, uint32_t rpv,
                       hipStream_t st)
 {
     const uint32_t grid = (n + 4 * rpv - 1) / (4 * rpv);
-    hipLaunchKernelGGL((k_w4a16_gemv_rows<MG, RG>), dim3(grid), dim3(256), 0, st,
-                       x, wp, ws, scale2, out, m, n, k, rpv);
+    if constexpr (MG == 1 && RG == 1) {
+        const uint32_t cus = cu_count();
+        if (cus != 0 && grid <= 3 * cus) {
+            launch_w4_st<1, 1, 4>(x, wp, ws, scale2, out, m, n, k, rpv, grid, st);
+            return;
+        }
+    }
+    launch_w4_st<MG, RG, 2>(x, wp, ws, scale2, out, m, n, k, rpv, grid, st);
 }
 
 // Live rows per wave for narrow weights: 4, or 3 when that cuts the rows on
