@@ -460,7 +460,8 @@ def test_fp8_gemv_blockscale_batched_rows_bit_identical_to_single_row(n, k):
 # ---------------------------------------------------------------------------
 # NVFP4-weight GEMV, W4A16 (fp8_gemv_batch.rs names w4a16_gemv_batch8_rt2).
 @pytest.mark.parametrize("n,k", [(64, 64), (256, 96), (200, 352), (384, 1216), (5000, 224),
-                                 (6144, 5120), (17408, 512), (65600, 448), (65664, 1600)])
+                                 (3000, 2048), (6144, 5120), (17408, 512), (65600, 448),
+                                 (65664, 1600)])
 def test_w4a16_gemv_all_m(n, k):
     # k = 96 / 352 / 1216 / 224 / 448 / 1600 end 96 / 352 / 192 / 224 / 448 /
     # 64 elements into a 512-element window; k = 1216 (3 windows) ends on an
@@ -468,7 +469,9 @@ def test_w4a16_gemv_all_m(n, k):
     # 4 (6144, and 5000 with a ragged last workgroup, and the small n);
     # n >= 65536 takes 8 rows per wave (ragged last tiles), whose staged scale
     # pieces straddle the end of a row's scales at k = 448 and 1600.  m <= 4
-    # and m > 4 take the one- and two-group kernels.
+    # and m > 4 take the one- and two-group kernels; at m <= 4 the small
+    # narrow grids (all but n = 17408) run four register stages, with 1, 3,
+    # 4 (k = 2048) and 10 windows.
     wp, ws, s2 = synth.gemv_nvfp4_weight(n, k, "cpu", shape_id=0)
     x = synth.gemv_acts_bf16(8, k, "cpu", shape_id=6)
     wpd, wsd = dev(wp), dev(ws)
