@@ -278,12 +278,11 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 // are loaded ahead, and the four partial tiles are added in a fixed order at
 // the end.
 //
-// A workgroup has a capacity of RC rows (8, or a multiple of 16 up to 80:
-// RC / 16 MFMA row tiles) of which the first rpw are live; rows past them
-// read zero.  The launcher sizes rpw so that the grid is a whole number of
-// workgroups per CU.  RC = 8 halves the work unit (N = 6144: 768
-// workgroups, three per CU); the MFMA's weight rows 8..15 then read an
-// all-zero LDS row.  XR activation rows are loaded per segment (M <= XR);
+// A workgroup has a capacity of RC rows (8, 12, or a multiple of 16 up to
+// 80: RC / 16 MFMA row tiles) of which the first rpw are live; rows past
+// them read zero.  The launcher sizes rpw so that the grid is a whole number of
+// workgroups per CU.  Below 16 rows (RC = 8 or 12) the MFMA's weight rows
+// RC..15 read an all-zero LDS row.  XR activation rows are loaded per segment (M <= XR);
 // the rows past them likewise read a zero row.  None of RC, rpw, XR, D and
 // SEG changes any summation order.
 //
@@ -310,7 +309,8 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     // RC rows of capacity per workgroup, of which the first rpw are live
     // (rpw = RC with block scales, whose scale row must be the workgroup's)
     constexpr int R = RC;
-    static_assert(RC == 8 || (RC % 16 == 0 && RC <= 80), "8 or a multiple of 16 up to 80 rows");
+    static_assert(RC == 8 || (RC == 12 && SEG == 256) || (RC % 16 == 0 && RC <= 80),
+                  "8, 12 (256-element segments) or a multiple of 16 up to 80 rows");
     static_assert(XR == 2 || XR == 4 || XR == 8 || XR == 16, "2, 4, 8 or 16 activation rows");
     static_assert(SEG == 256 || (SEG == 128 && !BS), "256-element segments, or 128 without block scales");
     // MFMA weight tiles of 16 rows (R = 8: one, its rows 8..15 zero)
@@ -523,11 +523,15 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 // weight byte; but a narrow grid is short (a few microseconds), and when
 // some CUs get one workgroup more than others those CUs set the time (N =
 // 17408 in 32-row workgroups is 544 of them on 256 CUs: 26.0 us, against
-// 20.1 us for N = 16384's 512).  So above M = 2 the grid is a whole number
-// j of workgroups per CU, each with rpw = ceil(N / (j CUs)) live rows in a
-// capacity of 8 or a multiple of 16 rows (up to 80), and j follows M:
-//   - M <= 2: 8 rows (the weight dominates; the 8-row unit already spreads
-//     evenly, and the activation pair is small);
+// 20.1 us for N = 16384's 512).  So the rows follow M:
+//   - M <= 2: 12 rows in a 12-row capacity (the weight dominates and the
+//     activation pair is small; at 12 rows the grid fits in the workgroups
+//     the CUs hold at once, where 8 rows needed a second partial round: N =
+//     17408, M = 1 / 2: 16.4 / 17.1 -> 16.2 / 16.6 us, N = 6144 equal or 1%
+//     faster);
+// and above M = 2 the grid is a whole number j of workgroups per CU, each
+// with rpw = ceil(N / (j CUs)) live rows in a capacity of 8 or a multiple of
+// 16 rows (up to 80), j following M:
 //   - M <= 4: about 16 rows per workgroup (N = 6144: 12 rows on 512
 //     workgroups, 8.4 -> 7.9 us);
 //   - M <= 8: two workgroups per CU (N = 17408: 34 rows, 21.5 -> 19.6 us;
@@ -545,10 +549,12 @@ struct GvSplit {
 static GvSplit gemv_split(uint32_t n, uint32_t m, bool bs)
 {
     const uint32_t cus = cu_count();
-    if (bs || m <= 2 || cus == 0) {
+    if (bs || cus == 0) {
         const uint32_t r = m <= 2 ? 8 : m <= 8 ? 16 : 32;
         return GvSplit{r, r};
     }
+    if (m <= 2)
+        return GvSplit{12, 12};
     const uint32_t div = cus * (m <= 4 ? 16 : 80);
     uint32_t j = (n + div - 1) / div;
     if (m > 4 && m <= 8 && j < 2)
@@ -566,7 +572,7 @@ constexpr bool ksplit_shape_ok()
 {
     if (BS)
         return RC == (XR <= 2 ? 8 : XR <= 8 ? 16 : 32);
-    return XR == 2 ? RC == 8 : XR == 4 ? RC <= 16 : RC >= 16;
+    return XR == 2 ? RC == 8 || RC == 12 : XR == 4 ? RC == 8 || RC == 16 : RC >= 16;
 }
 
 template <int RC, int XR, int D, bool BS, int SEG>
@@ -592,6 +598,10 @@ static hipError_t launch_ksplit_xr(const uint16_t *x, const uint8_t *w, const fl
         return hipErrorInvalidConfiguration;
     switch (sp.rc) {
     case 8: return launch_ksplit_rc<8, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+    case 12:
+        if constexpr (SEG == 256)
+            return launch_ksplit_rc<12, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
+        return hipErrorInvalidConfiguration;
     case 16: return launch_ksplit_rc<16, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
     case 32: return launch_ksplit_rc<32, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
     case 48: return launch_ksplit_rc<48, XR, D, BS, SEG>(x, w, rs, out, m, n, k, sp.rpw, st);
