@@ -293,11 +293,12 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 // branch, so the compiler counts the loads in flight exactly and waits only
 // for the stage it is about to use.
 // ---------------------------------------------------------------------------
-template <int RC, int NW, int NX>
+template <int RC, int NW, int NX, int NS>
 struct GvSegK {
     u32x4 w[NW];         // RC weight rows of the segment, 1 KB per instruction
     u32x4 x[NX];         // XR activation rows of the segment, 1 KB per instruction
-    float s[2];          // block scales of the segment's two K blocks (BS)
+    float s[NS][2];      // BS: per row tile, the block scales of the lane's row for
+                         // the segment's two K blocks
 };
 
 template <int RC, int XR, int D, bool BS, int SEG>
@@ -342,7 +343,16 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, 2 * m * k, 0x00020000);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
         (void *)rs, 0, BS ? 4 * (n / 128) * kbl : 4 * n, 0x00020000);
-    const uint32_t sbase = BS ? 4 * (row0 / 128) * kbl : 0;
+    // BS: the scale-grid offsets of the lane's weight row in each row tile
+    // (a workgroup's rows may span two 128-row scale blocks); dead rows
+    // read zero scales, which multiply their zero partials.
+    constexpr int NS = BS ? NT : 1;
+    uint32_t sbo[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+        const uint32_t rl = 16 * t + col, r = row0 + rl;
+        sbo[t] = BS && rl < rpw && r < n ? 4 * (r / 128) * kbl : OOB;
+    }
 
     // weight instruction j: row WRPI j + lane / WCH, bytes 16 (lane % WCH)
     // .. +15 of the segment
@@ -363,14 +373,17 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         xofs[i] = r < m ? 2 * (r * k + 8 * xc) : OOB;
     }
 
-    auto load = [&](GvSegK<RC, NW, NX> &g, uint32_t seg) {
+    auto load = [&](GvSegK<RC, NW, NX, NS> &g, uint32_t seg) {
         const bool live = seg < s_end;
         const uint32_t kb = seg * SEG;
         if constexpr (BS) {
-            g.s[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                sr, live ? sbase + 8 * seg : OOB, 0, 0));
-            g.s[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                sr, live && 2 * seg + 1 < kbl ? sbase + 8 * seg + 4 : OOB, 0, 0));
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                g.s[t][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    sr, live ? sbo[t] + 8 * seg : OOB, 0, 0));
+                g.s[t][1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    sr, live && 2 * seg + 1 < kbl ? sbo[t] + 8 * seg + 4 : OOB, 0, 0));
+            }
         }
         const bool wlive = live && kb + 16 * wc < k;
 #pragma unroll
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
             g.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                 xr, xlive ? xofs[i] + 2 * kb : OOB, 0, 0));
     };
-    auto stash = [&](const GvSegK<RC, NW, NX> &g) {
+    auto stash = [&](const GvSegK<RC, NW, NX, NS> &g) {
 #pragma unroll
         for (int j = 0; j < NW; ++j)
             *reinterpret_cast<u32x4 *>(&sw[wave][(WRPI * j + wr0) * WPITCH + 16 * wc]) = g.w[j];
@@ -420,12 +433,15 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
         p_pend[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    float s_pend = 0.f;
+    float s_pend[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+        s_pend[t] = 0.f;
 
     // D stages in flight.  The loop is unrolled by D so every stage is a
     // statically named variable: stage d holds segment seg + d, and is
     // reloaded with segment seg + d + D as soon as it has been stashed.
-    GvSegK<RC, NW, NX> g[D];
+    GvSegK<RC, NW, NX, NS> g[D];
 #pragma unroll
     for (int d = 0; d < D; ++d)
         load(g[d], s_beg + d);
@@ -442,8 +458,12 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         // The second block of a segment may lie past K (K an odd number of
         // 128-blocks); its scale then reads zero and its zero partial adds
         // nothing.
-        const float s_lo = g[d].s[0];
-        const float s_hi = g[d].s[1];
+        float s_lo[NS], s_hi[NS];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            s_lo[t] = g[d].s[t][0];
+            s_hi[t] = g[d].s[t][1];
+        }
         load(g[d], seg + D);
         f32x4 p[2][NT];     // partials of the segment's two K blocks (BS)
 #pragma unroll
@@ -470,9 +490,9 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
                     // The order of the additions is still block by block
                     // along K.
                     if (u == 0)
-                        fold_block(acc[t], s_pend, p_pend[t]);
+                        fold_block(acc[t], s_pend[t], p_pend[t]);
                     if (u == 2)
-                        fold_block(acc[t], s_lo, p[0][t]);
+                        fold_block(acc[t], s_lo[t], p[0][t]);
                 } else {
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), blo, acc[t], 0, 0, 0);
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), bhi, acc[t], 0, 0, 0);
@@ -481,15 +501,16 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
         }
         if constexpr (BS) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t) {
                 p_pend[t] = p[1][t];
-            s_pend = s_hi;
+                s_pend[t] = s_hi[t];
+            }
         }
     }
     if constexpr (BS)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            fold_block(acc[t], s_pend, p_pend[t]);
+            fold_block(acc[t], s_pend[t], p_pend[t]);
 
     // Fixed-order reduction of the four K-quarter partial tiles.
     if (wave > 0)
@@ -538,8 +559,10 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 //     N = 6144: 12 rows, 9.6 -> 9.1 us);
 //   - M <= 16: one workgroup per CU while its rows fit (N = 17408: 68 rows,
 //     26.0 -> 22.0 us; N = 12288: 48 rows, 18.9 -> 16.4 us).
-// Block scales need a workgroup's rows inside one 128-row scale block, so
-// that path keeps 8, 16 or 32 rows.  (Loading the activations straight
+// The block-scaled form takes the same rows up to M = 4 (each lane reads the
+// scales of its own row's 128-row block); above M = 4 its 256-element
+// segments would double the registers of the larger workgroups, so it keeps
+// 16 or 32 rows there.  (Loading the activations straight
 // into MFMA operand registers instead of through LDS was slower at every
 // M > 2: each load instruction then touches 16 rows.)  None of these
 // choices changes any row's summation order.
@@ -549,7 +572,7 @@ struct GvSplit {
 static GvSplit gemv_split(uint32_t n, uint32_t m, bool bs)
 {
     const uint32_t cus = cu_count();
-    if (bs || cus == 0) {
+    if (cus == 0 || (bs && m > 4)) {
         const uint32_t r = m <= 2 ? 8 : m <= 8 ? 16 : 32;
         return GvSplit{r, r};
     }
@@ -570,8 +593,8 @@ static GvSplit gemv_split(uint32_t n, uint32_t m, bool bs)
 template <int RC, int XR, bool BS>
 constexpr bool ksplit_shape_ok()
 {
-    if (BS)
-        return RC == (XR <= 2 ? 8 : XR <= 8 ? 16 : 32);
+    if (BS && XR > 4)
+        return RC == (XR == 8 ? 16 : 32);
     return XR == 2 ? RC == 8 || RC == 12 : XR == 4 ? RC == 8 || RC == 16 : RC >= 16;
 }
 
