@@ -559,10 +559,10 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
 //     N = 6144: 12 rows, 9.6 -> 9.1 us);
 //   - M <= 16: one workgroup per CU while its rows fit (N = 17408: 68 rows,
 //     26.0 -> 22.0 us; N = 12288: 48 rows, 18.9 -> 16.4 us).
-// The block-scaled form takes the same rows up to M = 4 (each lane reads the
-// scales of its own row's 128-row block); above M = 4 its 256-element
-// segments would double the registers of the larger workgroups, so it keeps
-// 16 or 32 rows there.  (Loading the activations straight
+// The block-scaled form takes the same rows (each lane reads the scales of
+// its own row's 128-row block), except that above M = 4 its 256-element
+// segments would double the registers of the larger workgroups: there it
+// takes them only up to 16 (M <= 8) or 32 rows, else 16 or 32 rows.  (Loading the activations straight
 // into MFMA operand registers instead of through LDS was slower at every
 // M > 2: each load instruction then touches 16 rows.)  None of these
 // choices changes any row's summation order.
@@ -571,14 +571,16 @@ struct GvSplit {
 };
 static GvSplit gemv_split(uint32_t n, uint32_t m, bool bs)
 {
+    const uint32_t fixed = m <= 2 ? 8 : m <= 8 ? 16 : 32;
     const uint32_t cus = cu_count();
-    if (cus == 0 || (bs && m > 4)) {
-        const uint32_t r = m <= 2 ? 8 : m <= 8 ? 16 : 32;
-        return GvSplit{r, r};
-    }
+    if (cus == 0)
+        return GvSplit{fixed, fixed};
     if (m <= 2)
         return GvSplit{12, 12};
-    const uint32_t div = cus * (m <= 4 ? 16 : 80);
+    // the largest capacity: 80 rows, or 16 / 32 for the block-scaled form
+    // above M = 4
+    const uint32_t cap = m <= 4 ? 16 : bs ? fixed : 80;
+    const uint32_t div = cus * cap;
     uint32_t j = (n + div - 1) / div;
     if (m > 4 && m <= 8 && j < 2)
         j = 2;
@@ -594,7 +596,7 @@ template <int RC, int XR, bool BS>
 constexpr bool ksplit_shape_ok()
 {
     if (BS && XR > 4)
-        return RC == (XR == 8 ? 16 : 32);
+        return XR == 8 ? RC == 16 : RC == 16 || RC == 32;
     return XR == 2 ? RC == 8 || RC == 12 : XR == 4 ? RC == 8 || RC == 16 : RC >= 16;
 }
 
