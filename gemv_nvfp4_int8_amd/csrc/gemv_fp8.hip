@@ -308,7 +308,6 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_ksplit(
     uint32_t m, uint32_t n, uint32_t k, uint32_t rpw)
 {
     // RC rows of capacity per workgroup, of which the first rpw are live
-    // (rpw = RC with block scales, whose scale row must be the workgroup's)
     constexpr int R = RC;
     static_assert(RC == 8 || (RC == 12 && SEG == 256) || (RC % 16 == 0 && RC <= 80),
                   "8, 12 (256-element segments) or a multiple of 16 up to 80 rows");
