@@ -320,10 +320,12 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
 
     // Epilogue: C[i][j] = bf16(acc * (as[i] * ws[j])).  Lane rows
     // i = ib + 32*ti, columns j = jb + 32*tj + 8*q + c (c = 0..3); a shifted
-    // tile stores only rows >= m0 and columns >= n0, element by element.
+    // tile stores only rows >= m0 and columns >= n0.  With N % 8 == 0 the
+    // shift n0 - n0e is a multiple of 8, so every 8-column unit lies wholly
+    // on one side of n0 and shifted tiles take the staged path too.
     const uint32_t ib = m0e + wm * 128 + (lane & 31);
     const uint32_t jb = n0e + wn * 128 + 4 * (lane >> 5);
-    if (vec_ok && m0e == m0 && n0e == n0) {
+    if (vec_ok) {
         float sa[4];
         f32x4 sw[4][4];
 #pragma unroll
@@ -365,16 +367,26 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
         // treating the reads as independent of those writes.
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         const int p = lane & 15;
-        uint16_t *const obase = out + (size_t)(m0 + wm * 128) * N + n0 + wn * 128;
+        const uint32_t rb = m0e + wm * 128, cb = n0e + wn * 128;
+        uint16_t *const obase = out + (size_t)rb * N + cb;
+        // Two copies of the loop: the per-store row / column test of a
+        // shifted tile cost 1.5% when every tile ran it.
+        auto store_block = [&](auto guarded) {
 #pragma unroll 4
-        for (int it = 0; it < 32; ++it) {
-            const int r = 4 * it + (lane >> 4);
-            u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * 256 + 16 * p);
-            if (r & 1)
-                v = (u32x4){v[2], v[3], v[0], v[1]};
-            const int lc = p ^ ((r & 31) >> 1);
-            *reinterpret_cast<u32x4 *>(obase + (size_t)r * N + 8 * lc) = v;
-        }
+            for (int it = 0; it < 32; ++it) {
+                const int r = 4 * it + (lane >> 4);
+                u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * 256 + 16 * p);
+                if (r & 1)
+                    v = (u32x4){v[2], v[3], v[0], v[1]};
+                const int lc = p ^ ((r & 31) >> 1);
+                if (!decltype(guarded)::value || (rb + r >= m0 && cb + 8 * lc >= n0))
+                    *reinterpret_cast<u32x4 *>(obase + (size_t)r * N + 8 * lc) = v;
+            }
+        };
+        if (m0e == m0 && n0e == n0)
+            store_block(std::false_type());
+        else
+            store_block(std::true_type());
     } else {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {

@@ -282,11 +282,13 @@ def test_fp8_gemm_rowscale_matches_oracle(m, n, k):
 # More 256 x 256 tiles than compute units (289 tiles: a second wave of 33
 # workgroups; 289 % 8 = 1 leaves one tile outside the XCD remap); shifted last
 # tiles with N % 8 != 0 (element-wise epilogue) and with N % 8 == 0 (staged
-# epilogue on the whole tiles, element-wise on the shifted ones).  The
+# epilogue with a row / 8-column guard), shifted in M, in N or in both.  The
+# output starts filled with a sentinel, so a skipped store fails.  The
 # oracle computes a sample of rows and columns (each output depends only on
 # its own row pair): random ones plus every row and column of the last two
 # tile rows and columns.
-@pytest.mark.parametrize("m,n,k", [(4352, 4352, 640), (4200, 4100, 640), (4200, 4104, 1280)])
+@pytest.mark.parametrize("m,n,k", [(4352, 4352, 640), (4200, 4100, 640), (4200, 4104, 1280),
+                                   (4200, 4352, 640), (4352, 4104, 640)])
 def test_fp8_gemm_rowscale_many_tiles_matches_oracle(m, n, k):
     a = _bf16_rows((m, k), 63 + m)
     w = _bf16_rows((n, k), 64 + n, std=0.02)
