@@ -18,6 +18,8 @@
 #include "gemm_common.hpp"
 #include "qp_launch.hpp"
 
+#include <type_traits>
+
 namespace qp {
 
 constexpr int W4_BM = 128, W4_BN = 128;
@@ -394,15 +396,16 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     // j = jb + 16*tj + c (c = 0..3).
     const uint32_t ib = m0e + wm * RW + r16;
     const uint32_t jb = n0e + wn * 80 + 4 * g;
-    if (WM == 2 && m0e == m0 && n0e == n0 && N % 8 == 0 &&
-        reinterpret_cast<uintptr_t>(out) % 16 == 0) {
+    if (WM == 2 && N % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) {
         // Stored from the MFMA layout, each store would put 32 bytes into
         // each of 16 rows.  Instead the workgroup stages its 256 x 160 BF16
         // tile in LDS (rows of 320 bytes at a 336-byte pitch, which spreads
         // a write's 16 rows over the banks; rows 0-127 in B0, 128-255 in
         // B1: the last stage ended with every DMA landed and a barrier) and
         // stores it row-contiguously, 64 consecutive 16-byte chunks (about
-        // three rows) per instruction.
+        // three rows) per instruction.  A shifted tile stores only rows
+        // >= m0 and chunks at columns >= n0 (with N % 8 == 0 the shift is a
+        // multiple of 8 columns, so no chunk straddles n0).
         uint8_t *const ep = wm == 0 ? B0 : B1;
 #pragma unroll
         for (int ti = 0; ti < NA; ++ti)
@@ -416,15 +419,23 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
                                            2 * (wn * 80 + 16 * tj + 4 * g)) = pk;
             }
         __syncthreads();
-        uint16_t *const obase = out + (size_t)m0 * N + n0;
+        uint16_t *const obase = out + (size_t)m0e * N + n0e;
+        // whole tiles run a copy of the loop without the row / column test
+        auto store_tile = [&](auto guarded) {
 #pragma unroll 4
-        for (int i = 0; i < WB_TN / 8; ++i) {
-            const int idx = threadIdx.x + 256 * i;      // chunk: row idx / 20, 16 bytes idx % 20
-            const int row = idx / (WB_TN / 8), ch = idx % (WB_TN / 8);
-            const uint8_t *src = (row < 128 ? B0 : B1) + (row & 127) * W4_EPITCH + 16 * ch;
-            *reinterpret_cast<u32x4 *>(obase + (size_t)row * N + 8 * ch) =
-                *reinterpret_cast<const u32x4 *>(src);
-        }
+            for (int i = 0; i < WB_TN / 8; ++i) {
+                const int idx = threadIdx.x + 256 * i;  // chunk: row idx / 20, 16 bytes idx % 20
+                const int row = idx / (WB_TN / 8), ch = idx % (WB_TN / 8);
+                const uint8_t *src = (row < 128 ? B0 : B1) + (row & 127) * W4_EPITCH + 16 * ch;
+                if (!decltype(guarded)::value || (m0e + row >= m0 && n0e + 8 * ch >= n0))
+                    *reinterpret_cast<u32x4 *>(obase + (size_t)row * N + 8 * ch) =
+                        *reinterpret_cast<const u32x4 *>(src);
+            }
+        };
+        if (m0e == m0 && n0e == n0)
+            store_tile(std::false_type());
+        else
+            store_tile(std::true_type());
         return;
     }
     const bool fast = m0e == m0 && n0e == n0 && N % 4 == 0 &&

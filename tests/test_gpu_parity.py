@@ -225,11 +225,13 @@ def test_int8_gemm_is_the_f32_fold_of_the_exact_partials(m, n, k):
 # Shapes cover both kernels: the 128 x 128 one and the 256 x 160 one (M >= 256,
 # N >= 160, K % 256 == 0) with one tile (256, 160), shifted last tiles
 # (300 x 330, 520 x 500), one stage, an even and an odd stage count, and
-# N % 4 != 0 (element-wise epilogue).  Whole tiles with N % 8 == 0 store
-# through the LDS-staged epilogue (256 x 160; 520 x 488 beside shifted ones).
+# N % 4 != 0 (element-wise epilogue).  With N % 8 == 0 every tile stores
+# through the LDS-staged epilogue, shifted ones with a row / 8-column test
+# (256 x 160; 520 x 488 shifted in M and N, 520 x 480 in M only, 512 x 488 in
+# N only).  The output starts filled with a sentinel, so a skipped store fails.
 @pytest.mark.parametrize("m,n,k", [(64, 96, 256), (33, 70, 160), (200, 300, 1024), (5, 130, 4096),
                                    (256, 160, 256), (300, 330, 512), (520, 500, 1280), (257, 162, 768),
-                                   (520, 488, 512)])
+                                   (520, 488, 512), (520, 480, 512), (512, 488, 512)])
 def test_w4a4_gemm_matches_oracle(m, n, k):
     a = _bf16_rows((m, k), 51 + m)
     w = _bf16_rows((n, k), 52 + n, std=0.02)
