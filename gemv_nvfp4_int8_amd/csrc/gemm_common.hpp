@@ -29,18 +29,23 @@ __device__ __forceinline__ int mfma32_row(int r, int lane)
 // one weight panel against every activation tile.
 constexpr uint32_t GROUP_M = 8;
 
-// Tile of linear workgroup id v.
-__device__ __forceinline__ void tile_coords_of(uint32_t v, uint32_t mtiles, uint32_t ntiles,
-                                               uint32_t &tm, uint32_t &tn)
+// Tile at position id of the banded order.
+__device__ __forceinline__ void banded_tile(uint32_t id, uint32_t mtiles, uint32_t ntiles,
+                                            uint32_t &tm, uint32_t &tn)
 {
-    uint32_t total = mtiles * ntiles;
-    uint32_t id = xcd_remap(v, total);
     uint32_t per_band = GROUP_M * ntiles;
     uint32_t band = id / per_band, rem = id % per_band;
     uint32_t band_m0 = band * GROUP_M;
     uint32_t rows = mtiles - band_m0 < GROUP_M ? mtiles - band_m0 : GROUP_M;
     tm = band_m0 + rem % rows;
     tn = rem / rows;
+}
+
+// Tile of linear workgroup id v.
+__device__ __forceinline__ void tile_coords_of(uint32_t v, uint32_t mtiles, uint32_t ntiles,
+                                               uint32_t &tm, uint32_t &tn)
+{
+    banded_tile(xcd_remap(v, mtiles * ntiles), mtiles, ntiles, tm, tn);
 }
 
 __device__ __forceinline__ void tile_coords(uint32_t mtiles, uint32_t ntiles,

@@ -132,13 +132,27 @@ __global__ __launch_bounds__(256) void k_fp8_gemm_rowscale(
 // stores it row by row, 4 rows of 256 bytes per instruction.
 // The MFMA is issued with zero scale operands, which selects the unscaled
 // encoding (identical results to unit E8M0 scales, at lower power).
+//
+// NT is the number of 32-column W tiles per wave: 4 for the 256 x 256 tile,
+// 2 for a 256 x 128 half tile (W panels of 128 rows, 16 KB of their slot).
+// One workgroup runs per CU, so time goes by rounds of one tile per CU; a
+// grid whose last round is at most half full runs that round's tiles as
+// half tiles in a second launch (NT = 2), on twice as many CUs.  Every
+// output still takes its whole K sum from one wave in the same order, so
+// the results do not depend on the split.  The NT = 4 launch covers the
+// first nfull tiles of the banded order (tile_coords), the NT = 2 launch
+// the rest, workgroups 2i and 2i + 1 the halves of tile nfull + i.
 // ---------------------------------------------------------------------------
+template <int NT>
 __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
     const uint8_t *__restrict__ A, const float *__restrict__ as,
     const uint8_t *__restrict__ W, const float *__restrict__ ws,
     uint16_t *__restrict__ out, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t mtiles, uint32_t ntiles, uint32_t vec_ok)
+    uint32_t mtiles, uint32_t ntiles, uint32_t nfull, uint32_t vec_ok)
 {
+    static_assert(NT == 4 || NT == 2, "whole or half tiles");
+    constexpr int TN = 64 * NT;        // tile columns = W panel rows
+    constexpr int WL = 2 * NT;         // DMA loads per wave of a W panel
     // The five slots are separate LDS variables: accesses to distinct
     // variables carry distinct alias scopes, so the compiler can see that
     // reading one slot need not wait for the DMA into another (with one
@@ -154,34 +168,45 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
     const int wm = wave & 1, wn = wave >> 1;
     const uint32_t nst = K / BIG_KB;
 
-    uint32_t tm, tn;
-    tile_coords(mtiles, ntiles, tm, tn);
-    const uint32_t m0 = tm * 256, n0 = tn * 256;
-    const uint32_t m0e = min(m0, M - 256), n0e = min(n0, N - 256);
+    uint32_t tm, tn, half = 0;
+    if (NT == 4) {
+        banded_tile(xcd_remap(blockIdx.x, nfull), mtiles, ntiles, tm, tn);
+    } else {
+        banded_tile(nfull + blockIdx.x / 2, mtiles, ntiles, tm, tn);
+        half = blockIdx.x & 1;
+    }
+    const uint32_t m0 = tm * 256, n0 = tn * 256 + 128 * half;
+    const uint32_t m0e = min(m0, M - 256), n0e = min(n0, N - TN);
     const uint8_t *const a_rows = A + (size_t)(m0e + 64 * wave) * K;
-    const uint8_t *const w_rows = W + (size_t)(n0e + 64 * wave) * K;
+    const uint8_t *const w_rows = W + (size_t)(n0e + (TN / 4) * wave) * K;
 
-    // DMA of one panel (the layout of dma_stage): instruction j of wave w
-    // fills kilobyte 8w+j = rows 64w + 8j + lane/8; lane's physical chunk
-    // lane%8 holds logical chunk (lane%8) ^ swz(row) with swz(row) =
-    // ((j & 1) << 2) | (lane >> 4).  The lane part of the source offset
-    // therefore takes two values (even / odd j); the rest is uniform.
+    // DMA of one panel of L kilobytes per wave (8 for A and whole-tile W
+    // panels, 4 for half-tile W panels): instruction j of wave w fills
+    // kilobyte Lw+j = rows 8(Lw+j) + lane/8, a multiple of 32 plus
+    // 8j + lane/8; lane's physical chunk lane%8 holds logical chunk
+    // (lane%8) ^ swz(row) with swz(row) = ((j & 1) << 2) | (lane >> 4).  The
+    // lane part of the source offset therefore takes two values (even / odd
+    // j); the rest is uniform.
     uint32_t dvo[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e)
         dvo[e] = (uint32_t)(lane >> 3) * K + 16u * ((lane & 7) ^ ((e << 2) | (lane >> 4)));
     // Panel of stage st; stages past the end reload the last one (in bounds,
     // never read) so that every stage issues the same loads.
-    auto dma_panel = [&](const uint8_t *rows, uint32_t st, uint8_t *slot) {
+    auto dma_panel = [&](const uint8_t *rows, uint32_t st, uint8_t *slot, auto nl) {
+        constexpr int L = decltype(nl)::value;
         const uint8_t *src = rows + (st < nst ? st : nst - 1) * BIG_KB;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < L; ++j)
             __builtin_amdgcn_global_load_lds(src + (size_t)(8 * j) * K + dvo[j & 1],
-                                             (lds_void *)(slot + 1024 * (8 * wave + j)), 16, 0, 0);
+                                             (lds_void *)(slot + 1024 * (L * wave + j)), 16, 0, 0);
     };
+    const std::integral_constant<int, 8> LA;
+    const std::integral_constant<int, WL> LW;
 
-    // LDS fragment reads: tile row wm*128 + 32t + lane%32 of a slot, logical
-    // chunk c at physical c ^ (((lane%32) >> 1) & 7).  The lane part of the
+    // LDS fragment reads: A row wm*128 + 32t + lane%32 of a slot (W row
+    // wn*32*NT + 32t + lane%32), logical chunk c at physical
+    // c ^ (((lane%32) >> 1) & 7).  The lane part of the
     // address depends on c only; t and the wave's half are immediate or
     // uniform offsets.
     const int g = lane >> 5;
@@ -204,33 +229,35 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
         asm volatile("" : "+v"(lo[0]), "+v"(lo[1]), "+v"(lo[2]), "+v"(lo[3]));
     };
     struct Frags {
-        i32x8 a[4], w[4];
+        i32x8 a[4], w[NT];
     };
     auto read_frags = [&](Frags &f, const uint8_t *la, const uint8_t *lw, int ks) {
         const uint32_t o0 = lo[2 * ks], o1 = lo[2 * ks + 1];
         const uint8_t *pa0 = la + wm * 128 * BIG_KB + o0, *pa1 = la + wm * 128 * BIG_KB + o1;
-        const uint8_t *pw0 = lw + wn * 128 * BIG_KB + o0, *pw1 = lw + wn * 128 * BIG_KB + o1;
+        const uint8_t *pw0 = lw + wn * 32 * NT * BIG_KB + o0, *pw1 = lw + wn * 32 * NT * BIG_KB + o1;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             u32x4 a0 = *reinterpret_cast<const u32x4 *>(pa0 + 32 * BIG_KB * t);
             u32x4 a1 = *reinterpret_cast<const u32x4 *>(pa1 + 32 * BIG_KB * t);
-            u32x4 w0 = *reinterpret_cast<const u32x4 *>(pw0 + 32 * BIG_KB * t);
-            u32x4 w1 = *reinterpret_cast<const u32x4 *>(pw1 + 32 * BIG_KB * t);
             f.a[t] = (i32x8){(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            f.w[t] = (i32x8){(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
-                             (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+            if (t < NT) {
+                u32x4 w0 = *reinterpret_cast<const u32x4 *>(pw0 + 32 * BIG_KB * t);
+                u32x4 w1 = *reinterpret_cast<const u32x4 *>(pw1 + 32 * BIG_KB * t);
+                f.w[t < NT ? t : 0] = (i32x8){(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
+                                              (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+            }
         }
     };
     // acc[ti][tj]: C^T block of A tile ti (32 rows of C) and W tile tj
-    f32x16 acc[4][4];
-    // MFMAs [lo, hi) of the 16 (4 x 4 tiles) of one K step
+    f32x16 acc[4][NT];
+    // MFMAs [lo, hi) of the 4 * NT of one K step
     auto mfma_range = [&](const Frags &f, int lo_, int hi_) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 4 * NT; ++i)
             if (i >= lo_ && i < hi_)
-                acc[i / 4][i % 4] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    f.w[i % 4], f.a[i / 4], acc[i / 4][i % 4], 0, 0, 0, 0, 0, 0);
+                acc[i / NT][i % NT] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.w[i % NT], f.a[i / NT], acc[i / NT][i % NT], 0, 0, 0, 0, 0, 0);
     };
     auto interleave = [&](int n_mfma, int n_ds, int n_vmem) {
         // n_ds LDS reads, two after each of the first MFMAs (early, so they
@@ -242,7 +269,10 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (2 * i < n_ds)
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            if (i < n_vmem)
+            const int nv = (i + 1) * n_vmem / n_mfma - i * n_vmem / n_mfma;   // 0, 1 or 2
+            if (nv >= 1)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (nv >= 2)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
@@ -258,14 +288,15 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
 
     // Stage st, X = (st, K step 0) already in registers, A(st) and W(st) in
     // slots ca and cw, A(st+1) and W(st+1) due in na and nw:
-    //   16 MFMAs on X + LDS reads of Y = (st, K step 1)
+    //   4 NT MFMAs on X + LDS reads of Y = (st, K step 1)
     //   sync: A(st+1) and W(st+1) have landed (only A(st+2) may still be
     //         in flight: 8 loads per wave), and every wave has finished
     //         reading ca and cw
     //   DMA of W(st+2) into ca and A(st+3) into cw
-    //   16 MFMAs on Y + LDS reads of X = (st+1, K step 0), issued over the
-    //      first 8 so that they have returned before the next stage needs
-    //      them, and the 16 DMA loads, one per MFMA
+    //   4 NT MFMAs on Y + LDS reads of X = (st+1, K step 0), issued two
+    //      per MFMA from the first so that they have returned before the
+    //      next stage needs them, and the 8 + WL DMA loads spread evenly
+    //      (one per MFMA for whole tiles)
     // The slots are passed as the LDS variables themselves so that every
     // access names its slot statically.
     Frags X, Y;
@@ -273,30 +304,31 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
                      const uint8_t *nw) {
         launder();
         read_frags(Y, ca, cw, 1);
-        mfma_range(X, 0, 16);
-        interleave(16, 16, 0);
+        mfma_range(X, 0, 4 * NT);
+        interleave(4 * NT, 8 + 2 * NT, 0);
         sync_stage(std::integral_constant<int, 8>());
-        dma_panel(w_rows, st + 2, ca);
-        dma_panel(a_rows, st + 3, cw);
+        dma_panel(w_rows, st + 2, ca, LW);
+        dma_panel(a_rows, st + 3, cw, LA);
         read_frags(X, na, nw, 0);
-        mfma_range(Y, 0, 16);
-        interleave(16, 16, 16);
+        mfma_range(Y, 0, 4 * NT);
+        interleave(4 * NT, 8 + 2 * NT, 8 + WL);
         __builtin_amdgcn_sched_barrier(0);
     };
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
-    dma_panel(a_rows, 0, S0);
-    dma_panel(w_rows, 0, S1);
-    dma_panel(a_rows, 1, S2);
-    dma_panel(w_rows, 1, S3);
-    dma_panel(a_rows, 2, S4);
-    sync_stage(std::integral_constant<int, 24>());
+    dma_panel(a_rows, 0, S0, LA);
+    dma_panel(w_rows, 0, S1, LW);
+    dma_panel(a_rows, 1, S2, LA);
+    dma_panel(w_rows, 1, S3, LW);
+    dma_panel(a_rows, 2, S4, LA);
+    // A0 and W0 landed: A1, W1 and A2 may be in flight
+    sync_stage(std::integral_constant<int, 16 + WL>());
     launder();
     read_frags(X, S0, S1, 0);
     uint32_t st = 0;
@@ -324,30 +356,33 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
     // shift n0 - n0e is a multiple of 8, so every 8-column unit lies wholly
     // on one side of n0 and shifted tiles take the staged path too.
     const uint32_t ib = m0e + wm * 128 + (lane & 31);
-    const uint32_t jb = n0e + wn * 128 + 4 * (lane >> 5);
+    const uint32_t jb = n0e + wn * 32 * NT + 4 * (lane >> 5);
     if (vec_ok) {
         float sa[4];
-        f32x4 sw[4][4];
+        f32x4 sw[NT][4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
             sa[ti] = as[ib + 32 * ti];
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj)
+        for (int tj = 0; tj < NT; ++tj)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 sw[tj][q] = *reinterpret_cast<const f32x4 *>(ws + jb + 32 * tj + 8 * q);
-        // Stage the wave's 128 x 128 block in slot `wave` (every wave has
-        // finished reading the slots and its DMA has landed), 256 bytes per
-        // row.  8-byte unit u of row r sits at u ^ (r % 32): the 32 lanes of
-        // a half-wave (rows r % 32 = 0..31, one unit each) then write 32
-        // different units of their rows, all 64 banks.
+        // Stage the wave's 128 x 32NT block in slot `wave` (every wave has
+        // finished reading the slots and its DMA has landed), RB = 64NT
+        // bytes per row.  8-byte unit u of row r sits at u ^ x(r), with
+        // x(r) = r % 32 for 256-byte rows and (r % 32) / 2 for 128-byte
+        // rows: the 32 lanes of a half-wave (rows r % 32 = 0..31, one unit
+        // each) then write 32 different 8-byte places of the 256-byte bank
+        // row, all 64 banks.
+        constexpr int RB = 64 * NT, XS = NT == 4 ? 0 : 1;
         __syncthreads();
         uint8_t *const ep = wave == 0 ? S0 : wave == 1 ? S1 : wave == 2 ? S2 : S3;
         const int r5 = lane & 31, hh = lane >> 5;
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < NT; ++tj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f32x16 &c = acc[ti][tj];
@@ -356,29 +391,31 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
                                     c[4 * q + 1] * (sa[ti] * sw[tj][q][1]));
                     pk[1] = pk_bf16(c[4 * q + 2] * (sa[ti] * sw[tj][q][2]),
                                     c[4 * q + 3] * (sa[ti] * sw[tj][q][3]));
-                    *reinterpret_cast<u32x2 *>(ep + (r5 + 32 * ti) * 256 + 8 * ((8 * tj + 2 * q + hh) ^ r5)) = pk;
+                    *reinterpret_cast<u32x2 *>(ep + (r5 + 32 * ti) * RB + 8 * ((8 * tj + 2 * q + hh) ^ (r5 >> XS))) = pk;
                 }
         }
-        // Read back 16-byte units p (physical) of 4 rows per instruction:
-        // they hold logical units p ^ ((r % 32) >> 1), with their two
-        // 8-byte halves swapped in odd rows.  Other lanes of the wave wrote
-        // them; a wave's LDS operations execute in order, and the
-        // wavefront-scope fence (no instruction) keeps the compiler from
+        // Read back the PU = RB / 16 physical 16-byte units p of 64 / PU
+        // rows per instruction: unit p holds logical unit p ^ (x(r) / 2),
+        // its two 8-byte halves swapped where x(r) is odd.  Other lanes of
+        // the wave wrote them; a wave's LDS operations execute in order, and
+        // the wavefront-scope fence (no instruction) keeps the compiler from
         // treating the reads as independent of those writes.
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        const int p = lane & 15;
-        const uint32_t rb = m0e + wm * 128, cb = n0e + wn * 128;
+        constexpr int PU = RB / 16, RPI = 64 / PU;
+        const int p = lane & (PU - 1);
+        const uint32_t rb = m0e + wm * 128, cb = n0e + wn * 32 * NT;
         uint16_t *const obase = out + (size_t)rb * N + cb;
         // Two copies of the loop: the per-store row / column test of a
         // shifted tile cost 1.5% when every tile ran it.
         auto store_block = [&](auto guarded) {
 #pragma unroll 4
-            for (int it = 0; it < 32; ++it) {
-                const int r = 4 * it + (lane >> 4);
-                u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * 256 + 16 * p);
-                if (r & 1)
+            for (int it = 0; it < 128 / RPI; ++it) {
+                const int r = RPI * it + lane / PU;
+                u32x4 v = *reinterpret_cast<const u32x4 *>(ep + r * RB + 16 * p);
+                const int x = (r & 31) >> XS;
+                if (x & 1)
                     v = (u32x4){v[2], v[3], v[0], v[1]};
-                const int lc = p ^ ((r & 31) >> 1);
+                const int lc = p ^ (x >> 1);
                 if (!decltype(guarded)::value || (rb + r >= m0 && cb + 8 * lc >= n0))
                     *reinterpret_cast<u32x4 *>(obase + (size_t)r * N + 8 * lc) = v;
             }
@@ -393,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void k_fp8_gemm_rowscale_big(
             const uint32_t gi = ib + 32 * ti;
             const float sai = as[gi];
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < NT; ++tj)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const uint32_t gj = jb + 32 * tj + 8 * (r >> 2) + (r & 3);
@@ -411,14 +448,30 @@ hipError_t launch_fp8_gemm_rowscale(const uint8_t *a, const float *as,
                                     uint32_t k, hipStream_t st)
 {
     if (k % BIG_KB == 0 && m >= 256 && n >= 256) {
-        uint32_t mt = (m + 255) / 256, nt = (n + 255) / 256;
+        const uint32_t mt = (m + 255) / 256, nt = (n + 255) / 256, tiles = mt * nt;
         // 16-byte output stores and column-scale loads need N % 8 == 0 and
         // aligned base pointers; otherwise every tile takes the element-wise
         // epilogue.
-        uint32_t vec_ok = n % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0 &&
-                          reinterpret_cast<uintptr_t>(ws) % 16 == 0;
-        hipLaunchKernelGGL(k_fp8_gemm_rowscale_big, dim3(mt * nt), dim3(256), 0, st,
-                           a, as, w, ws, out, m, n, k, mt, nt, vec_ok);
+        const uint32_t vec_ok = n % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0 &&
+                                reinterpret_cast<uintptr_t>(ws) % 16 == 0;
+        // One tile per CU at a time: a last round at most half full runs as
+        // twice as many half tiles (with the CU count unknown, no split).
+        const uint32_t cus = cu_count(), tail = cus ? tiles % cus : 0;
+        const uint32_t nfull = tail != 0 && 2 * tail <= cus ? tiles - tail : tiles;
+        if (nfull) {
+            hipLaunchKernelGGL(k_fp8_gemm_rowscale_big<4>, dim3(nfull), dim3(256), 0, st,
+                               a, as, w, ws, out, m, n, k, mt, nt, nfull, vec_ok);
+            count_launch();
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        if (nfull < tiles) {
+            hipLaunchKernelGGL(k_fp8_gemm_rowscale_big<2>, dim3(2 * (tiles - nfull)), dim3(256),
+                               0, st, a, as, w, ws, out, m, n, k, mt, nt, nfull, vec_ok);
+            count_launch();
+        }
+        return hipGetLastError();
     } else {
         uint32_t mt = (m + F8_BM - 1) / F8_BM, nt = (n + F8_BN - 1) / F8_BN;
         hipLaunchKernelGGL(k_fp8_gemm_rowscale, dim3(mt * nt), dim3(256), 0, st,

@@ -250,6 +250,8 @@ int quant_rowwise_fp8(const uint16_t *x, uint8_t *q, float *scale,
  *   C[i,j] = bf16( a_scale[i] * w_scale[j] * sum_t e4m3(a[i,t]) * e4m3(w[j,t]) ).
  *   a [m,k] E4M3, a_scale [m] F32, w [n,k] E4M3, w_scale [n] F32,
  *   out [m,n] BF16.  Requires k % 16 == 0.  Any m is served (no padding).
+ * Enqueues one kernel, or two when the last round of large tiles is thin
+ * enough to run as half tiles; the output bits are the same either way.
  * ---------------------------------------------------------------------- */
 int fp8_gemm_rowscale(const uint8_t *a, const float *a_scale, const uint8_t *w,
                       const float *w_scale, uint16_t *out, uint32_t m,

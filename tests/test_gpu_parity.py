@@ -306,6 +306,39 @@ def test_fp8_gemm_rowscale_many_tiles_matches_oracle(m, n, k):
     assert_gemm_close(host(out)[np.ix_(ri, ci)], ref, f"fp8 {m}x{n}x{k}")
 
 
+# One workgroup runs per CU, so a grid whose last round is at most half full
+# runs that round's tiles as 256 x 128 half tiles.  Each output still takes its
+# whole K sum in the same order, so results must not depend on the split: an
+# M = 2048 or 1900 call (8 x 48 tiles, the last 128 of the banded order split
+# into halves on 256 CUs) must equal, bit for bit, the same rows of an
+# M = 2304 call (9 x 48 tiles, last round 176 > 128: no split).  N = 12200
+# shifts the last half tile; N = 12196 (N % 8 != 0) takes the element-wise
+# epilogue; M = 1900 shifts the last tile row.
+@pytest.mark.parametrize("m,n", [(2048, 12200), (1900, 12200), (2048, 12196)])
+def test_fp8_gemm_half_tile_tail_is_bit_identical(m, n):
+    k, mref = 1280, 2304
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    tiles = lambda mm: -(-mm // 256) * -(-n // 256)
+    splits = lambda mm: 0 < tiles(mm) % cus <= cus // 2
+    if not (splits(m) and not splits(mref)):
+        pytest.skip(f"{cus} CUs: these shapes do not separate split and unsplit grids")
+    a = _bf16_rows((mref, k), 81)
+    w = _bf16_rows((n, k), 82, std=0.02)
+    oa, oas = oracle.quant_rowwise_fp8(bits(a))
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    t = lambda x: dev(torch.from_numpy(np.ascontiguousarray(x)))
+    ref = filled((mref, n), torch.bfloat16)
+    qp.fp8_gemm_rowscale(t(oa), t(oas), t(ow), t(ows), ref)
+    out = filled((m, n), torch.bfloat16)
+    qp.fp8_gemm_rowscale(t(oa[:m]), t(oas[:m]), t(ow), t(ows), out)
+    assert np.array_equal(host(out), host(ref)[:m])
+    rng = np.random.default_rng(m + n)
+    ri = np.union1d(rng.choice(m, 24, replace=False), np.arange(m - 8, m))
+    ci = np.union1d(rng.choice(n, 64, replace=False), np.arange(n - 300, n))
+    assert_gemm_close(host(out)[np.ix_(ri, ci)],
+                      oracle.fp8_gemm_rowscale(oa[ri], oas[ri], ow[ci], ows[ci]), f"fp8 {m}x{n}")
+
+
 def test_fp8_rowwise_proj_block_and_passthrough():
     m, n, k = 70, 256, 512
     cse = synth.fp8_block("cpu", m=m, n=n, k=k)
