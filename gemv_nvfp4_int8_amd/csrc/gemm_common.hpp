@@ -58,6 +58,21 @@ __device__ __forceinline__ void tile_coords(uint32_t mtiles, uint32_t ntiles,
 // XCD-aware order above; 1 = plain M-fast (workgroup id = tm + mtiles * tn,
 // consecutive workgroups share a weight panel); 2 = plain N-fast (consecutive
 // workgroups share an activation panel).
+// Tile at position id of order 0 (banded, without the XCD remap), 1 or 2.
+__device__ __forceinline__ void tile_in_order(uint32_t order, uint32_t id, uint32_t mtiles,
+                                              uint32_t ntiles, uint32_t &tm, uint32_t &tn)
+{
+    if (order == 1) {
+        tm = id % mtiles;
+        tn = id / mtiles;
+    } else if (order == 2) {
+        tn = id % ntiles;
+        tm = id / ntiles;
+    } else {
+        banded_tile(id, mtiles, ntiles, tm, tn);
+    }
+}
+
 __device__ __forceinline__ void tile_coords_order(uint32_t order, uint32_t mtiles,
                                                   uint32_t ntiles, uint32_t &tm, uint32_t &tn)
 {

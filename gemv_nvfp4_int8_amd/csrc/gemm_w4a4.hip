@@ -212,29 +212,46 @@ constexpr int WB_BUF = WB_SW + 256 * WB_NS;   // + 4 KB = 60 KB
 constexpr int W4_EPITCH = 2 * WB_TN + 16;     // epilogue staging: bytes per output row
 static_assert(128 * W4_EPITCH <= WB_BUF, "half the output tile fits one stage buffer");
 
-// WM waves along M (2 or 4) times 2 along N: a wave owns RW = 256 / WM rows
+// WM waves along M (2 or 4) times 2 along N: a wave owns RW = TM / WM rows
 // (NA = RW / 16 MFMA tiles) by 80 columns (5 tiles).  WM = 4 runs two waves
 // per SIMD (512 threads, at most 256 registers each).
-template <int WM>
+//
+// TM is the tile height: 256, or 128 for the half tiles of a thin last
+// round.  One workgroup runs per CU, so time goes by rounds of one tile per
+// CU; when the last round is at most half full, its tiles run in a second
+// launch as two 128 x 160 halves each (the first half on rows m0 .. m0+127),
+// on twice the CUs, with the same stage buffer layout (A rows 128-255 and
+// their scales unused).  Each output keeps its whole K sum, in the same
+// order, so results do not depend on the split.  The TM = 256 launch takes
+// the first nfull tiles of the launch's tile order, the TM = 128 launch the
+// rest, workgroups 2i and 2i + 1 the halves of tile nfull + i.
+template <int WM, int TM = WB_TM>
 __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     const uint8_t *__restrict__ Ap, const uint8_t *__restrict__ Asc,
     const uint8_t *__restrict__ Wp, const uint8_t *__restrict__ Wsc,
     uint16_t *__restrict__ out, float s2, uint32_t M, uint32_t N, uint32_t K,
-    uint32_t mtiles, uint32_t ntiles, uint32_t order)
+    uint32_t mtiles, uint32_t ntiles, uint32_t nfull, uint32_t order)
 {
+    static_assert(TM == WB_TM || TM == WB_TM / 2, "whole or half tiles");
     constexpr int NW = 2 * WM;            // waves
-    constexpr int RW = WB_TM / WM;        // rows per wave
+    constexpr int RW = TM / WM;           // rows per wave
     constexpr int NA = RW / 16;           // A tiles per wave
-    constexpr int APW = 32 / NW;          // A packed kilobytes per wave
+    constexpr int APW = TM / 8 / NW;      // A packed kilobytes per wave
     // Two stage buffers as separate LDS variables (distinct alias scopes:
     // reading one need not wait for the DMA into the other).
     __shared__ __attribute__((aligned(1024))) uint8_t B0[WB_BUF];
     __shared__ __attribute__((aligned(1024))) uint8_t B1[WB_BUF];
 
-    uint32_t tm, tn;
-    tile_coords_order(order, mtiles, ntiles, tm, tn);
-    const uint32_t m0 = tm * WB_TM, n0 = tn * WB_TN;
-    const uint32_t m0e = min(m0, M - WB_TM), n0e = min(n0, N - WB_TN);
+    uint32_t tm, tn, half = 0;
+    if (TM == WB_TM) {
+        tile_in_order(order, order == 0 ? xcd_remap(blockIdx.x, nfull) : blockIdx.x,
+                      mtiles, ntiles, tm, tn);
+    } else {
+        tile_in_order(order, nfull + blockIdx.x / 2, mtiles, ntiles, tm, tn);
+        half = blockIdx.x & 1;
+    }
+    const uint32_t m0 = tm * WB_TM + TM * half, n0 = tn * WB_TN;
+    const uint32_t m0e = min(m0, M - TM), n0e = min(n0, N - WB_TN);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % WM, wn = wave / WM;
@@ -256,7 +273,10 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     const uint8_t *const a_rows = Ap + (size_t)(m0e + 8 * APW * wave) * ldp;
     const uint8_t *const w_rows = Wp + (size_t)(n0e + 8 * wave) * ldp;
     const int sq = wave & 3;
-    const uint8_t *const as_row = Asc + (size_t)(m0e + 64 * sq + lane) * lds_;
+    // (half tiles: the scale rows past the tile's 128 land in the unused
+    // half of the region; rows past M reload row M - 1, in bounds)
+    const uint32_t asr = m0e + 64 * sq + lane;
+    const uint8_t *const as_row = Asc + (size_t)(TM == WB_TM || asr < M ? asr : M - 1) * lds_;
     const uint32_t wsr = n0e + 64 * sq + lane;
     const uint8_t *const ws_row = Wsc + (size_t)(wsr < N ? wsr : N - 1) * lds_;
     // Stage st into buffer B (stages past the end reload the last one: in
@@ -398,7 +418,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
     const uint32_t jb = n0e + wn * 80 + 4 * g;
     if (WM == 2 && N % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) {
         // Stored from the MFMA layout, each store would put 32 bytes into
-        // each of 16 rows.  Instead the workgroup stages its 256 x 160 BF16
+        // each of 16 rows.  Instead the workgroup stages its TM x 160 BF16
         // tile in LDS (rows of 320 bytes at a 336-byte pitch, which spreads
         // a write's 16 rows over the banks; rows 0-127 in B0, 128-255 in
         // B1: the last stage ended with every DMA landed and a barrier) and
@@ -406,7 +426,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
         // three rows) per instruction.  A shifted tile stores only rows
         // >= m0 and chunks at columns >= n0 (with N % 8 == 0 the shift is a
         // multiple of 8 columns, so no chunk straddles n0).
-        uint8_t *const ep = wm == 0 ? B0 : B1;
+        uint8_t *const ep = (wm * RW < 128 ? B0 : B1) + ((wm * RW) & 127) * W4_EPITCH;
 #pragma unroll
         for (int ti = 0; ti < NA; ++ti)
 #pragma unroll
@@ -423,7 +443,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a4_gemm_big(
         // whole tiles run a copy of the loop without the row / column test
         auto store_tile = [&](auto guarded) {
 #pragma unroll 4
-            for (int i = 0; i < WB_TN / 8; ++i) {
+            for (int i = 0; i < TM * (WB_TN / 8) / 256; ++i) {
                 const int idx = threadIdx.x + 256 * i;  // chunk: row idx / 20, 16 bytes idx % 20
                 const int row = idx / (WB_TN / 8), ch = idx % (WB_TN / 8);
                 const uint8_t *src = (row < 128 ? B0 : B1) + (row & 127) * W4_EPITCH + 16 * ch;
@@ -469,11 +489,28 @@ hipError_t launch_w4a4_gemm(const uint8_t *ap, const uint8_t *asc,
 {
     float s2 = sa2 * sw2;
     if (k % WB_KE == 0 && m >= (uint32_t)WB_TM && n >= (uint32_t)WB_TN) {
-        uint32_t mt = (m + WB_TM - 1) / WB_TM, nt = (n + WB_TN - 1) / WB_TN;
+        const uint32_t mt = (m + WB_TM - 1) / WB_TM, nt = (n + WB_TN - 1) / WB_TN;
+        const uint32_t tiles = mt * nt;
+        // One tile per CU at a time: a last round at most half full runs as
+        // twice as many half tiles (with the CU count unknown, no split).
+        const uint32_t cus = cu_count(), tail = cus ? tiles % cus : 0;
+        const uint32_t nfull = tail != 0 && 2 * tail <= cus ? tiles - tail : tiles;
         // WM = 2 (four waves, 128 x 80 each): two waves per SIMD (WM = 4)
         // measured slower at 4096 x 5120 x 17408 (778 vs 736 us)
-        hipLaunchKernelGGL(k_w4a4_gemm_big<2>, dim3(mt * nt), dim3(256), 0, st,
-                           ap, asc, wp, wsc, out, s2, m, n, k, mt, nt, order);
+        if (nfull) {
+            hipLaunchKernelGGL(k_w4a4_gemm_big<2>, dim3(nfull), dim3(256), 0, st,
+                               ap, asc, wp, wsc, out, s2, m, n, k, mt, nt, nfull, order);
+            count_launch();
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        if (nfull < tiles) {
+            hipLaunchKernelGGL((k_w4a4_gemm_big<2, WB_TM / 2>), dim3(2 * (tiles - nfull)), dim3(256),
+                               0, st, ap, asc, wp, wsc, out, s2, m, n, k, mt, nt, nfull, order);
+            count_launch();
+        }
+        return hipGetLastError();
     } else {
         uint32_t mt = (m + W4_BM - 1) / W4_BM, nt = (n + W4_BN - 1) / W4_BN;
         hipLaunchKernelGGL(k_w4a4_gemm, dim3(mt * nt), dim3(256), 0, st,

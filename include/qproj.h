@@ -189,6 +189,8 @@ int quantize_bf16_nvfp4(const uint16_t *x, uint8_t *packed, uint8_t *scale,
  * Each block's E4M3 scale is folded into its E2M1 operands (the product is
  * exact in FP16), so the contraction runs on FP16 MFMA with F32
  * accumulation and the per-block scaling costs no extra pass.
+ * Enqueues one kernel, or two when the last round of large tiles is thin
+ * enough to run as half tiles; the output bits are the same either way.
  * ---------------------------------------------------------------------- */
 int w4a4_gemm(const uint8_t *a_packed, const uint8_t *a_scale,
               const uint8_t *w_packed, const uint8_t *w_scale, uint16_t *out,

@@ -244,6 +244,38 @@ def test_w4a4_gemm_matches_oracle(m, n, k):
     assert_gemm_close(host(out), oracle.w4a4_gemm(ap, asc, wp, wsc, 1.0, sw2), f"w4a4 {m}x{n}x{k}")
 
 
+# The W4A4 GEMM runs a last round that is at most half full as 128 x 160 half
+# tiles (one workgroup per CU).  Each output keeps its K sum order, so an
+# M = 2304 or 2200 call (9 x 32 tiles: the last 32 split on 256 CUs) must
+# equal, bit for bit, the same rows of an M = 3328 call (13 x 32 tiles, last
+# round 160 > 128: no split).  M = 2200 shifts the last half tile;
+# N = 5122 (33 column tiles, N % 4 != 0) takes the element-wise epilogue.
+@pytest.mark.parametrize("m,n", [(2304, 5120), (2200, 5120), (2304, 5122)])
+def test_w4a4_gemm_half_tile_tail_is_bit_identical(m, n):
+    k, mref = 512, 3328
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    tiles = lambda mm: -(-mm // 256) * -(-n // 160)
+    splits = lambda mm: 0 < tiles(mm) % cus <= cus // 2
+    if not (splits(m) and not splits(mref)):
+        pytest.skip(f"{cus} CUs: these shapes do not separate split and unsplit grids")
+    a = _bf16_rows((mref, k), 91)
+    w = _bf16_rows((n, k), 92, std=0.02)
+    sw2 = synth.per_tensor_scale2(w)
+    ap, asc = oracle.quantize_bf16_nvfp4(bits(a), 1.0)
+    wp, wsc = oracle.quantize_bf16_nvfp4(bits(w), sw2)
+    t = lambda x: dev(torch.from_numpy(np.ascontiguousarray(x)))
+    ref = filled((mref, n), torch.bfloat16)
+    qp.w4a4_gemm(t(ap), t(asc), t(wp), t(wsc), ref, 1.0, sw2)
+    out = filled((m, n), torch.bfloat16)
+    qp.w4a4_gemm(t(ap[:m]), t(asc[:m]), t(wp), t(wsc), out, 1.0, sw2)
+    assert np.array_equal(host(out), host(ref)[:m])
+    rng = np.random.default_rng(m + n)
+    ri = np.union1d(rng.choice(m, 24, replace=False), np.arange(m - 8, m))
+    ci = np.union1d(rng.choice(n, 64, replace=False), np.arange(n - 200, n))
+    assert_gemm_close(host(out)[np.ix_(ri, ci)],
+                      oracle.w4a4_gemm(ap[ri], asc[ri], wp[ci], wsc[ci], 1.0, sw2), f"w4a4 {m}x{n}")
+
+
 @pytest.mark.parametrize("m,n,k", [(32, 128, 256), (256, 160, 512)])
 def test_w4a4_every_scale_code_and_nibble(m, n, k):
     # All 16 E2M1 codes against all finite E4M3 scale codes, on both kernels.
