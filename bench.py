@@ -11,9 +11,10 @@ whose total footprint exceeds 1 GiB per shape so that the 256 MB Infinity
 Cache cannot hold them.
 
 The same line carries:
-  roofline      the dominant kernel (the M=16 lm_head GEMV, N=152064) timed
-                alone with HIP events on the launch stream, its algorithmic
-                bytes per launch, and the fraction of the 8 TB/s HBM peak;
+  roofline      the dominant kernel, the lm_head GEMV (N=152064) over the
+                step's M mix, timed alone with HIP events on the launch
+                stream, its algorithmic bytes per launch, and the fraction of
+                the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same step;
   secondary     every other row of the hot path at its own workload size:
                 quantizers / requantizers in GB/s against HBM, the three
@@ -241,7 +242,8 @@ def main():
     dom_bytes = sum(gemv_bytes(d["m"], 152064, 5120) for d in dom) / len(dom)
     dom_us = sum(d["us"] for d in dom) / len(dom)
     roofline = {"bound": "hbm",
-                "kernel": "k_fp8_gemv_rows<2,1> (N=152064, K=5120, M in {1,2,8,16})",
+                "kernel": "lm_head FP8 GEMV (N=152064, K=5120, M in {1,2,8,16}): "
+                          "k_fp8_gemv_ksplit at M <= 2, k_fp8_gemv_rows above",
                 "achieved": round(dom_bytes / (dom_us * 1e-6) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom_bytes / (dom_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

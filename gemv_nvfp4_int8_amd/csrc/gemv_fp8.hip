@@ -26,14 +26,16 @@
 //    part, against ~5 TB/s for the 16 rows x 64 bytes an MFMA-shaped load
 //    would touch.  Each wave transposes its bytes through a private LDS tile
 //    into MFMA operand layout.
-//  * Two work splits, chosen from N alone (see gemv_wide): wide weights give
-//    each wave its own rows over all of K, with the activation segment staged
-//    once per workgroup in LDS and shared by its four waves; narrow weights
-//    split K over the four waves of a workgroup (everything wave-private) and
-//    add the partial tiles in a fixed order.  The narrow kernel's launch
-//    shape (8 or 16 rows per workgroup, activation rows loaded, segments in
-//    flight) may follow M, but no summation order depends on M, so every
-//    output row is bit-identical to an M = 1 call on that row.
+//  * Two work splits (see gemv_rows): wide weights above M = 2 give each
+//    wave its own rows over all of K, with the activation segment staged
+//    once per workgroup in LDS and shared by its four waves; narrow weights,
+//    and wide ones at M <= 2, split K over the four waves of a workgroup
+//    (everything wave-private) and add the partial tiles in a fixed order.
+//    The row-owning kernel sums each row in the same K quarters, added in
+//    the same order, so the two kernels give identical bits.  The K-split
+//    kernel's launch shape (rows per workgroup, activation rows loaded,
+//    segments in flight) may follow M, but no summation order depends on M
+//    or N: every output row is bit-identical to an M = 1 call on that row.
 #include "qp_device.hpp"
 #include "qp_launch.hpp"
 
@@ -179,6 +181,22 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 #pragma unroll
     for (int t = 0; t < T; ++t)
         p_pend[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    // The K quarters of the narrow kernel (per segments each, ending on
+    // 256-element boundaries): acc holds the current quarter's sum, tot the
+    // closed quarters' sums added in order, ((q0 + q1) + q2) + q3, with
+    // empty trailing quarters adding +0.  A row's summation order is then
+    // the narrow kernel's, so its bits do not depend on which kernel runs.
+    const uint32_t per = ((k + 255) / 256 + 3) / 4;
+    f32x4 tot[T];
+    uint32_t closed = 0, q_end = per;
+    auto close_quarter = [&]() {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            tot[t] = closed == 0 ? acc[t] : tot[t] + acc[t];
+            acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        ++closed;
+    };
 
     GvSeg<T> g[D];
 #pragma unroll
@@ -200,6 +218,20 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
             g[d] = g[d + 1];
         if (seg + D < nseg)
             load(g[D - 1], seg + D);
+        if (seg == q_end) {
+            // a new quarter: the previous one's pending block folds into
+            // its own sum first
+            if constexpr (BS) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    fold_block(acc[t], s_pend, p_pend[t]);
+                    p_pend[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                }
+                s_pend = 0.f;
+            }
+            close_quarter();
+            q_end += per;
+        }
         __syncthreads();
         f32x4 p[2][T];      // partials of the segment's two K blocks (BS)
 #pragma unroll
@@ -252,6 +284,8 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
 #pragma unroll
         for (int t = 0; t < T; ++t)
             fold_block(acc[t], s_pend, p_pend[t]);
+    while (closed < 4)
+        close_quarter();
 
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -263,7 +297,7 @@ __global__ __launch_bounds__(256) void k_fp8_gemv_rows(
                 uint32_t mm = 4u * grp + i;
                 if (mm < m)
                     out[(size_t)mm * n + nn] =
-                        (uint16_t)f32_to_bf16(BS ? acc[t][i] : acc[t][i] * sc);
+                        (uint16_t)f32_to_bf16(BS ? tot[t][i] : tot[t][i] * sc);
             }
         }
     }
@@ -666,6 +700,13 @@ static void launch_gemv_rows(const uint16_t *x, const uint8_t *w, const float *r
 // weights (lm_head-class) give every CU several row-split workgroups; narrow
 // ones split K inside the workgroup to keep enough waves streaming.
 static bool gemv_wide(uint32_t n) { return n >= 65536u; }
+// The row-owning kernel serves wide weights except at M <= 2, where the
+// K-split kernel reads them faster (lm_head, M = 1 / 2: 115.4 -> 110.1 /
+// 116.0 -> 112.5 us row-scaled, 116.3 -> 111.4 / 116.6 -> 114.6 us
+// block-scaled; at M = 4 and 8 it is slower, its many small workgroups each
+// reading the activation rows).  Both kernels sum every row in the same
+// order, so the choice changes no bits.
+static bool gemv_rows(uint32_t n, uint32_t m) { return gemv_wide(n) && m > 2; }
 
 // Segments in flight per wave for the K-split kernel: two once the grid has
 // several workgroups per CU (measured: N = 17408 gains 4-5% at every M,
@@ -688,7 +729,7 @@ hipError_t launch_fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
                                     const float *rs, uint16_t *out, uint32_t m,
                                     uint32_t n, uint32_t k, hipStream_t st)
 {
-    if (gemv_wide(n)) {
+    if (gemv_rows(n, m)) {
         launch_gemv_rows<2, 1, false>(x, w, rs, out, m, n, k, st);
     } else {
         const hipError_t e = launch_gemv_narrow<false>(x, w, rs, out, m, n, k, st);
@@ -704,7 +745,7 @@ hipError_t launch_fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
                                       const float *grid, uint16_t *out, uint32_t m,
                                       uint32_t n, uint32_t k, hipStream_t st)
 {
-    if (gemv_wide(n)) {
+    if (gemv_rows(n, m)) {
         launch_gemv_rows<2, 1, true>(x, w, grid, out, m, n, k, st);
     } else {
         const hipError_t e = launch_gemv_narrow<true>(x, w, grid, out, m, n, k, st);

@@ -407,7 +407,12 @@ def test_fp8_gemv_rowscale_all_m(n, k):
         assert_gemv_close(host(out), oracle.fp8_gemv_rowscale(bits(x[:m]), ow, ows), f"gemv m={m}")
 
 
-@pytest.mark.parametrize("n,k", [(300, 512), (17408, 5120)])
+# N >= 65536 runs the row-owning kernel above M = 2 and the K-split kernel
+# at M <= 2, so there the invariant also holds across the two kernels: K =
+# 2560 gives four non-empty K quarters (the last short), 1040 a partial last
+# segment and an empty last quarter, 256 three empty quarters.
+@pytest.mark.parametrize("n,k", [(300, 512), (17408, 5120), (65552, 2560), (65552, 1040),
+                                 (65600, 256)])
 def test_fp8_gemv_batched_rows_bit_identical_to_single_row(n, k):
     """The pages' invariant for the batched GEMV (fp8_gemv_batch.rs,
     dense_gemv_fp8w_batch2): each row of an M-row call equals, bit for bit,
@@ -422,10 +427,29 @@ def test_fp8_gemv_batched_rows_bit_identical_to_single_row(n, k):
         qp.fp8_gemv_rowscale(x[i:i + 1], wq, ws, o)
         singles.append(o)
     single = torch.cat(singles)
-    for m in (2, 8, 16):
+    for m in (2, 3, 8, 16):
         o = empty((m, n), torch.bfloat16)
         qp.fp8_gemv_rowscale(x[:m], wq, ws, o)
         assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
+
+
+# Both FP8 GEMV kernels sum every row in the same order (K quarters ending on
+# 256-element boundaries, added in order), so a weight row's output does not
+# depend on N either: the first 17408 rows of a wide weight (row-owning
+# kernel above M = 2) equal, bit for bit, the same rows run as a narrow
+# weight (K-split kernel).
+@pytest.mark.parametrize("k", [2560, 1040, 256])
+def test_fp8_gemv_wide_and_narrow_kernels_agree_bit_for_bit(k):
+    n, nn = 65552, 17408
+    w = synth.gemv_weight_bf16(n, k, "cpu", shape_id=6)
+    ow, ows = oracle.quant_rowwise_fp8(bits(w))
+    wq, ws = dev(torch.from_numpy(ow)), dev(torch.from_numpy(ows))
+    x = dev(synth.gemv_acts_bf16(16, k, "cpu", shape_id=6))
+    for m in (1, 2, 3, 8, 16):
+        wide, narrow = empty((m, n), torch.bfloat16), empty((m, nn), torch.bfloat16)
+        qp.fp8_gemv_rowscale(x[:m], wq, ws, wide)
+        qp.fp8_gemv_rowscale(x[:m], wq[:nn], ws[:nn], narrow)
+        assert torch.equal(wide[:, :nn].view(torch.int16), narrow.view(torch.int16)), m
 
 
 @pytest.mark.parametrize("n,k", [(70000, 512), (65552, 1040), (37, 1040), (12300, 1040)])
@@ -507,7 +531,7 @@ def test_fp8_gemv_blockscale_every_code_and_extreme_scales(n, k):
     assert_gemv_close(host(out), oracle.fp8_gemv_blockscale(bits(x), w, grid), "block gemv codes")
 
 
-@pytest.mark.parametrize("n,k", [(384, 640), (17408, 5120), (65536, 5120)])
+@pytest.mark.parametrize("n,k", [(384, 640), (17408, 5120), (65536, 5120), (65664, 640)])
 def test_fp8_gemv_blockscale_batched_rows_bit_identical_to_single_row(n, k):
     """The pages' invariant for w8a16_gemv_batch4 (fp8_gemv_batch.rs): each
     row of an M-row call equals, bit for bit, the single-row call."""
@@ -520,10 +544,26 @@ def test_fp8_gemv_blockscale_batched_rows_bit_identical_to_single_row(n, k):
         qp.fp8_gemv_blockscale(x[i:i + 1], wd, gd, o)
         singles.append(o)
     single = torch.cat(singles)
-    for m in (2, 4, 16):
+    for m in (2, 3, 4, 16):
         o = empty((m, n), torch.bfloat16)
         qp.fp8_gemv_blockscale(x[:m], wd, gd, o)
         assert torch.equal(o.view(torch.int16), single[:m].view(torch.int16)), m
+
+
+# The block-scaled form's kernels also share every row's summation order:
+# the first 12416 rows of a wide weight equal the same rows run narrow
+# (K = 640: an odd number of 128-blocks, an empty last K quarter).
+@pytest.mark.parametrize("k", [5120, 640])
+def test_fp8_gemv_blockscale_wide_and_narrow_kernels_agree_bit_for_bit(k):
+    n, nn = 65664, 12416
+    w, grid = synth.gemv_block_weight(n, k, "cpu", shape_id=2)
+    wd, gd = dev(w), dev(grid)
+    x = dev(synth.gemv_acts_bf16(16, k, "cpu", shape_id=7))
+    for m in (1, 2, 3, 8, 16):
+        wide, narrow = empty((m, n), torch.bfloat16), empty((m, nn), torch.bfloat16)
+        qp.fp8_gemv_blockscale(x[:m], wd, gd, wide)
+        qp.fp8_gemv_blockscale(x[:m], wd[:nn], gd[:nn // 128], narrow)
+        assert torch.equal(wide[:, :nn].view(torch.int16), narrow.view(torch.int16)), m
 
 
 # ---------------------------------------------------------------------------
