@@ -608,8 +608,11 @@ static GvSplit gemv_split(uint32_t n, uint32_t m, bool bs)
     const uint32_t cus = cu_count();
     if (cus == 0)
         return GvSplit{fixed, fixed};
+    // M <= 2: 12 rows (N = 17408: 1451 workgroups, all resident at once);
+    // wide weights 16 (lm_head, M = 2: 112.1 -> 110.8 us; block-scaled
+    // M = 1 / 2: 110.9 -> 109.7 / 114.4 -> 111.5 us; 32 and 48 rows slower)
     if (m <= 2)
-        return GvSplit{12, 12};
+        return n >= 65536u ? GvSplit{16, 16} : GvSplit{12, 12};
     // the largest capacity: 80 rows, or 16 / 32 for the block-scaled form
     // above M = 4
     const uint32_t cap = m <= 4 ? 16 : bs ? fixed : 80;
@@ -630,7 +633,7 @@ constexpr bool ksplit_shape_ok()
 {
     if (BS && XR > 4)
         return XR == 8 ? RC == 16 : RC == 16 || RC == 32;
-    return XR == 2 ? RC == 8 || RC == 12 : XR == 4 ? RC == 8 || RC == 16 : RC >= 16;
+    return XR == 2 ? RC == 8 || RC == 12 || RC == 16 : XR == 4 ? RC == 8 || RC == 16 : RC >= 16;
 }
 
 template <int RC, int XR, int D, bool BS, int SEG>
@@ -695,10 +698,10 @@ static void launch_gemv_rows(const uint16_t *x, const uint8_t *w, const float *r
                        x, w, rs, out, m, n, k);
 }
 
-// Work-split choice: it depends on n only (never on m), which keeps every
-// row's summation order, and so its bits, the same for every m.  Wide
-// weights (lm_head-class) give every CU several row-split workgroups; narrow
-// ones split K inside the workgroup to keep enough waves streaming.
+// Work-split choice.  Wide weights (lm_head-class) give every CU several
+// row-split workgroups; narrow ones split K inside the workgroup to keep
+// enough waves streaming.  The two kernels sum every row in the same order,
+// so the choice, which may follow m, never changes a row's bits.
 static bool gemv_wide(uint32_t n) { return n >= 65536u; }
 // The row-owning kernel serves wide weights except at M <= 2, where the
 // K-split kernel reads them faster (lm_head, M = 1 / 2: 115.4 -> 110.1 /
