@@ -282,7 +282,9 @@ int fp8_rowwise_proj(int fmt, const uint8_t *w, const float *w_scale,
  * 1 <= m <= 16 (else QP_ERR_RANGE); k % 16 == 0, n*k and m*n < 2^31 and
  * 2*m*k < 2^31 (else QP_ERR_SHAPE).  The weight is streamed from memory
  * once for all m rows, and every output row is bit-identical to the m == 1
- * call on that row.
+ * call on that row.  A row's K summation order depends on k alone, so an
+ * output is also bit-identical across calls with different n (a weight's
+ * first rows called as a weight of their own).
  * ---------------------------------------------------------------------- */
 int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
                       const float *row_scale, uint16_t *out, uint32_t m,
@@ -302,7 +304,7 @@ int fp8_gemv_rowscale(const uint16_t *x, const uint8_t *w,
  * block is summed in F32 and added to the running F32 sum with one FMA by
  * its scale; the BF16 rounding happens once at the end.  The weight is
  * streamed once for all m rows, and every output row is bit-identical to the
- * m == 1 call on that row.
+ * m == 1 call on that row, and across calls with different n.
  * ---------------------------------------------------------------------- */
 int fp8_gemv_blockscale(const uint16_t *x, const uint8_t *w,
                         const float *block_scale, uint16_t *out, uint32_t m,
